@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA forward operator on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--decode-steps D] [--no-cpu-baseline]
+
+One step is one kda_chunk_fwd over the 128K-token workload (B=1, H=32,
+T=131072, d_k=d_v=128, bf16 q/k/v, fp32 gates, random initial state,
+chunk 64), inputs resident in HBM. After the prefill steps, the decode
+workload (64 sequences x 32 heads, fp32 state cache, D successive
+kda_decode_step calls with fresh inputs per step) is timed the same way.
+
+Prints ONE JSON line: prefill Mtokens/s as `value`, its roofline (HBM bytes
+and MFMA FLOPs of the algorithm), the decode us/step with its HBM roofline,
+and the fp64 CPU oracle timed on a bounded sample of the same inputs.
+Timing uses HIP events recorded on the stream the kernels are launched on.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+C = 64
+
+
+def prefill_bytes(T, H, K, V, N, in_bytes=2, out_bytes=2, s0=True, sT=True):
+    """Algorithmic HBM bytes of one prefill: q, k, v, log_alpha, beta read
+    once, o written once, initial state read, final state written."""
+    per_tok_head = (2 * K + V) * in_bytes + 4 * K + 4 + V * out_bytes
+    return T * H * per_tok_head + N * H * K * V * 4 * (int(s0) + int(sT))
+
+
+def prefill_flops_per_token_head(K, V, c=C):
+    """FLOPs of the chunk algorithm per token-head, counting only triangles
+    that exist: K c(c-1) for A (strict lower), 2K c(c+1) for P and the WY
+    factor T (K e^G), 2V c(c+1) for T V and P U', c^3/3 for the triangular
+    inverse and 6 c K V for the three c x K x V products with the state."""
+    return (K * c * (c - 1) + 2 * K * c * (c + 1) + 2 * V * c * (c + 1)
+            + c ** 3 / 3 + 6 * c * K * V) / c
+
+
+def decode_bytes(B, H, K, V, in_bytes=2, out_bytes=2):
+    return B * H * (2 * K * V * 4 + 2 * K * in_bytes + K * 4 + 4 + V * in_bytes + V * out_bytes)
+
+
+def _cpu_threads():
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit():
+        return int(env)
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline_prefill(d, target_s=12.0):
+    """Time the fp64 oracle on the first tokens of the same 128K sequence, all
+    heads; the token count is grown until one run takes about target_s."""
+    import numpy as np
+    import oracle
+    threads = _cpu_threads()
+    tokens, elapsed = 256, 0.0
+    while True:
+        sub = {n: d[n][:tokens].float().cpu().numpy() for n in ("q", "k", "v", "log_alpha", "beta")}
+        s0 = d["initial_state"].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.prefill(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["beta"],
+                       np.array([0, tokens], np.int32), 1.0, s0, nthreads=threads)
+        elapsed = time.perf_counter() - t0
+        if elapsed >= target_s / 4 or tokens * 4 > d["q"].shape[0]:
+            break
+        tokens = min(d["q"].shape[0], int(tokens * max(2.0, min(16.0, target_s / 4 / max(elapsed, 1e-3)))))
+    return dict(value=tokens / elapsed / 1e6, unit="Mtokens/s", cores=threads, kind="oracle",
+                sample=f"fp64 oracle, first {tokens} tokens of the 128K sequence, all 32 heads, "
+                       f"{elapsed:.2f} s", seconds=elapsed)
+
+
+def cpu_baseline_decode(d, steps=3):
+    import numpy as np
+    import oracle
+    threads = _cpu_threads()
+    state = d["state"].cpu().numpy().astype(np.float64)
+    host = {n: d[n][:steps].float().cpu().numpy() for n in ("q", "k", "v", "log_alpha", "beta")}
+    t0 = time.perf_counter()
+    for s in range(steps):
+        oracle.decode(host["q"][s], host["k"][s], host["v"][s], host["log_alpha"][s],
+                      host["beta"][s], state, nthreads=threads)
+    el = time.perf_counter() - t0
+    return dict(value=el / steps * 1e6, unit="us/step", cores=threads, kind="oracle",
+                sample=f"fp64 oracle, {steps} decode steps of B=64, H=32, d=128")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of this many MiB (for HBM counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this operator benchmark runs on one GPU only; "
+                                   "--gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    from gated_delta_rule_10_amd import inputs, kda
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kda.load_library()
+    stream = torch.cuda.current_stream()
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    # ---- prefill: the 128K-token workload ----------------------------------
+    name = "long_128k"
+    w = inputs.WORKLOADS[name]
+    d = inputs.device_workload_inputs(name, device=dev)
+    T, H, K, V = d["q"].shape[0], w["H"], w["K"], w["V"]
+    N = d["cu_seqlens"].shape[0] - 1
+    o = torch.empty((T, H, V), dtype=torch.bfloat16, device=dev)
+    sT = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
+
+    def step():
+        kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["cu_seqlens"],
+                          initial_state=d["initial_state"], final_state=sT, o=o, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    total_ms = ev[0].elapsed_time(ev[-1])
+    ms = total_ms / args.steps
+    mtok = T / (ms / 1e3) / 1e6
+    nbytes = prefill_bytes(T, H, K, V, N)
+    flops = prefill_flops_per_token_head(K, V) * T * H
+    gbs = nbytes / (ms / 1e3) / 1e9
+    tflops = flops / (ms / 1e3) / 1e12
+    result = {
+        "metric": "KDA prefill Mtokens/s (H=32,d=128,T=128K) + decode us/step (B=64)",
+        "value": round(mtok, 3),
+        "unit": "Mtokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": os.environ.get("KDA_BENCH_DTYPE_LABEL", "bf16"),
+        "data": "synthetic (seeded torch draws on the device)",
+        "config": {"workload": "long_128k: 1 sequence x 131072 tokens, H=32, d_k=d_v=128, "
+                               "bf16 q/k/v, fp32 log_alpha/beta, fp32 initial+final state, "
+                               "chunk 64, o bf16",
+                   "global_batch": 1, "seq_len": T, "parallelism": "none (one GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "kda_chunk_fwd (one launch)",
+                     "algorithmic_bytes_per_launch": nbytes},
+        "mfma": {"achieved_tflops": round(tflops, 2), "peak_tflops": PEAK_BF16_TFLOPS,
+                 "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                 "flops_per_launch": flops, "count": "triangular-aware, C=64"},
+        "prefill_ms": {"min": round(min(per), 4), "max": round(max(per), 4),
+                       "median": round(sorted(per)[len(per) // 2], 4)},
+    }
+
+    cpu_d = None
+    if not args.no_cpu_baseline:
+        cpu_d = {n: d[n] for n in ("q", "k", "v", "log_alpha", "beta", "initial_state")}
+    del d, o, sT
+
+    # ---- decode: 64 sequences x 32 heads, fp32 cache -----------------------
+    if not args.prefill_only:
+        steps = args.decode_steps
+        dd = inputs.device_workload_inputs("decode_b64", device=dev, steps=steps)
+        Bd, Hd, Kd, Vd = 64, 32, 128, 128
+        state = dd["state"]
+        od = torch.empty((Bd, Hd, Vd), dtype=torch.bfloat16, device=dev)
+
+        def dstep(s):
+            kda.kda_decode_step(dd["q"][s], dd["k"][s], dd["v"][s], dd["log_alpha"][s],
+                                dd["beta"][s], state, o=od, stream=stream)
+
+        for s in range(min(args.warmup, steps)):
+            dstep(s)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for s in range(steps):
+            dstep(s)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        dbytes = decode_bytes(Bd, Hd, Kd, Vd)
+        dgbs = dbytes / (us / 1e6) / 1e9
+        result["decode"] = {
+            "value": round(us, 3), "unit": "us/step", "steps": steps,
+            "workload": "decode_b64: B=64, H=32, d_k=d_v=128, fp32 state cache (128 MiB), "
+                        "bf16 q/k/v/o, fresh inputs every step",
+            "roofline": {"bound": "hbm", "achieved": round(dgbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(dgbs / PEAK_HBM_GBS, 4),
+                         "algorithmic_bytes_per_launch": dbytes},
+        }
+        if cpu_d is not None:
+            result["decode"]["cpu_baseline"] = cpu_baseline_decode(dd)
+        del dd, state
+
+    if cpu_d is not None:
+        result["cpu_baseline"] = cpu_baseline_prefill(cpu_d)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,121 @@
+// C-ABI layer of libkda: host-side argument validation, kernel selection and
+// error mapping. Reads no device memory, allocates nothing and never
+// synchronises; see include/kda.h for the contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+
+#include "kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
+
+bool dtype_pair_ok(kda_dtype_t in, kda_dtype_t out) {
+    if (in == KDA_F32) return out == KDA_F32;
+    if (in == KDA_BF16) return out == KDA_BF16 || out == KDA_F32;
+    return false;
+}
+
+bool dtype_valid(kda_dtype_t d) { return d == KDA_F32 || d == KDA_BF16; }
+
+// Debug override of the prefill kernel for bf16 inputs: KDA_PREFILL_KERNEL=valu
+// selects the fp32 vector-ALU kernel. Read once per process.
+bool force_valu() {
+    static const bool f = [] {
+        const char *e = std::getenv("KDA_PREFILL_KERNEL");
+        return e && std::strcmp(e, "valu") == 0;
+    }();
+    return f;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char *kda_status_string(kda_status_t s) {
+    switch (s) {
+    case KDA_OK: return "KDA_OK: success";
+    case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: NULL or misaligned pointer, or size out of range";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: head dims must be 64 or 128, chunk size 64, dtype pair F32/F32, BF16/BF16 or BF16/F32";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace smaller than kda_chunk_fwd_workspace_size()";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP: kernel launch failed";
+    }
+    return "unknown kda_status_t";
+}
+
+size_t kda_chunk_fwd_workspace_size(int32_t N, int32_t T_total, int32_t H, int32_t d_k,
+                                    int32_t d_v, kda_dtype_t in_dtype) {
+    (void)N; (void)T_total; (void)H; (void)d_k; (void)d_v; (void)in_dtype;
+    return 0;  // every kernel keeps its intermediates on chip
+}
+
+kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                           const float *beta, const int32_t *cu_seqlens, int32_t N, int32_t T_total,
+                           int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t in_dtype,
+                           kda_dtype_t out_dtype, float scale, const float *initial_state,
+                           float *final_state, void *o, int32_t chunk_size, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+    if (N < 1 || H < 1 || T_total < 0) return KDA_ERR_INVALID_ARG;
+    if (!dtype_valid(in_dtype) || !dtype_valid(out_dtype)) return KDA_ERR_INVALID_ARG;
+    if (!cu_seqlens || !aligned16(cu_seqlens)) return KDA_ERR_INVALID_ARG;
+    if (T_total > 0) {
+        const void *req[] = {q, k, v, log_alpha, beta, o};
+        for (const void *p : req)
+            if (!p || !aligned16(p)) return KDA_ERR_INVALID_ARG;
+    }
+    if (!aligned16(initial_state) || !aligned16(final_state) || !aligned16(workspace))
+        return KDA_ERR_INVALID_ARG;
+    if (!head_dim_ok(d_k) || !head_dim_ok(d_v) || chunk_size != 64) return KDA_ERR_UNSUPPORTED;
+    if (!dtype_pair_ok(in_dtype, out_dtype)) return KDA_ERR_UNSUPPORTED;
+    // grid sizes are int32 on the device side
+    if (static_cast<int64_t>(N) * H * 16 > INT32_MAX) return KDA_ERR_INVALID_ARG;
+    if (static_cast<int64_t>(T_total) * H * (d_k > d_v ? d_k : d_v) > (int64_t(1) << 40))
+        return KDA_ERR_INVALID_ARG;
+    const size_t need = kda_chunk_fwd_workspace_size(N, T_total, H, d_k, d_v, in_dtype);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+
+    kda::PrefillArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = log_alpha; a.beta = beta; a.cu_seqlens = cu_seqlens;
+    a.s0 = initial_state; a.sT = final_state; a.o = o;
+    a.N = N; a.T = T_total; a.H = H; a.K = d_k; a.V = d_v; a.scale = scale;
+    a.in_dtype = in_dtype; a.out_dtype = out_dtype;
+    hipError_t e;
+    if (in_dtype == KDA_BF16 && !force_valu())
+        e = kda::launch_prefill_mfma(a, stream);
+    else
+        e = kda::launch_prefill_valu(a, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
+                             const float *beta, float *state_cache, const int32_t *slot_idx,
+                             void *o, int32_t B, int32_t H, int32_t d_k, int32_t d_v,
+                             int32_t num_slots, kda_dtype_t in_dtype, kda_dtype_t out_dtype,
+                             float scale, hipStream_t stream) {
+    if (B < 1 || H < 1 || num_slots < 1) return KDA_ERR_INVALID_ARG;
+    if (!dtype_valid(in_dtype) || !dtype_valid(out_dtype)) return KDA_ERR_INVALID_ARG;
+    const void *req[] = {q, k, v, log_alpha, beta, state_cache, o};
+    for (const void *p : req)
+        if (!p || !aligned16(p)) return KDA_ERR_INVALID_ARG;
+    if (!aligned16(slot_idx)) return KDA_ERR_INVALID_ARG;
+    if (!slot_idx && B > num_slots) return KDA_ERR_INVALID_ARG;
+    if (static_cast<int64_t>(B) * H > INT32_MAX) return KDA_ERR_INVALID_ARG;
+    if (!head_dim_ok(d_k) || !head_dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
+    if (!dtype_pair_ok(in_dtype, out_dtype)) return KDA_ERR_UNSUPPORTED;
+
+    kda::DecodeArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = log_alpha; a.beta = beta; a.state = state_cache;
+    a.slot_idx = slot_idx; a.o = o; a.B = B; a.H = H; a.K = d_k; a.V = d_v;
+    a.slots = num_slots; a.scale = scale; a.in_dtype = in_dtype; a.out_dtype = out_dtype;
+    return kda::launch_decode(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

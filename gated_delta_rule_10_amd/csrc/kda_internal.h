@@ -1,0 +1,44 @@
+// Internal launch interface between the C-ABI layer (kda_api.cpp) and the
+// HIP kernels. Not installed; the public interface is include/kda.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kda.h"
+
+namespace kda {
+
+struct PrefillArgs {
+    const void *q, *k, *v;       // [T, H, K|K|V] in_dtype
+    const float *g;              // log alpha [T, H, K]
+    const float *beta;           // [T, H]
+    const int32_t *cu_seqlens;   // [N + 1] device
+    const float *s0;             // [N, H, K, V] or nullptr
+    float *sT;                   // [N, H, K, V] or nullptr
+    void *o;                     // [T, H, V] out_dtype
+    int32_t N, T, H, K, V;
+    float scale;
+    kda_dtype_t in_dtype, out_dtype;
+};
+
+struct DecodeArgs {
+    const void *q, *k, *v;   // [B, H, K|K|V]
+    const float *g;          // [B, H, K]
+    const float *beta;       // [B, H]
+    float *state;            // [slots, H, K, V]
+    const int32_t *slot_idx; // [B] or nullptr
+    void *o;                 // [B, H, V]
+    int32_t B, H, K, V, slots;
+    float scale;
+    kda_dtype_t in_dtype, out_dtype;
+};
+
+// Each launcher enqueues its kernel(s) on `stream` and returns the launch
+// status (hipGetLastError after the launch).
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_prefill_valu(const PrefillArgs &a, hipStream_t stream);
+hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream);
+
+}  // namespace kda

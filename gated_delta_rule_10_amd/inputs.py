@@ -21,6 +21,12 @@ only), q, k, v, x, y, initial state):
 
 bf16 values are carried in float32 containers (exact) plus their raw 16-bit
 patterns, so the oracle reads exactly the numbers the GPU receives.
+
+Two generators follow this recipe: a numpy one (PCG64, for small cases built
+on the host) and a torch one that draws directly on the target device
+(`device_*`, for the 128K-token and larger workloads, where host generation
+takes minutes). A given seed gives different numbers on the two, so every
+comparison feeds the same drawn tensors to both sides.
 """
 
 from __future__ import annotations
@@ -40,6 +46,9 @@ __all__ = [
     "varlen_lengths",
     "WORKLOADS",
     "workload_inputs",
+    "device_prefill_inputs",
+    "device_decode_inputs",
+    "device_workload_inputs",
 ]
 
 
@@ -220,3 +229,93 @@ def workload_inputs(name: str, steps: Optional[int] = None):
     if lengths is None:
         lengths = varlen_lengths(rng, n_seqs, lo, hi, total)
     return prefill_inputs(seed=-1, lengths=lengths, rng=rng, **w)
+
+
+# --- torch generator drawing on the target device ------------------------
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def device_prefill_inputs(seed: int, lengths: Sequence[int], H: int, K: int, V: int,
+                          in_dtype: str = "bf16", decay_scale: float = 0.1,
+                          init: str = "zero", device="cuda") -> dict:
+    """The prefill recipe drawn with torch on `device`.
+
+    Returns a dict of tensors: q, k, v (bf16 or fp32), log_alpha, beta (fp32),
+    cu_seqlens (int32), initial_state (fp32 or None).
+    """
+    torch = _torch()
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    lengths = [int(x) for x in lengths]
+    N, T = len(lengths), int(sum(lengths))
+    dt = torch.bfloat16 if in_dtype == "bf16" else torch.float32
+
+    def normal(*shape):
+        return torch.randn(*shape, generator=gen, device=device, dtype=torch.float32)
+
+    def unit(x):
+        return x / torch.linalg.vector_norm(x, dim=-1, keepdim=True).clamp_min(1e-30)
+
+    q = unit(normal(T, H, K)).to(dt)
+    k = unit(normal(T, H, K)).to(dt)
+    v = normal(T, H, V).to(dt)
+    x = normal(T, H, K)
+    log_alpha = -torch.logaddexp(x, torch.zeros((), device=device)) * decay_scale
+    del x
+    beta = torch.sigmoid(normal(T, H))
+    s0 = None
+    if init != "zero":
+        s0 = 0.02 * normal(N, H, K, V)
+        if init == "odd_zero":
+            s0[1::2] = 0.0
+    cu = torch.zeros(N + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+    return dict(q=q, k=k, v=v, log_alpha=log_alpha.contiguous(), beta=beta,
+                cu_seqlens=cu.to(device), initial_state=s0)
+
+
+def device_decode_inputs(seed: int, steps: int, B: int, H: int, K: int, V: int,
+                         slots: Optional[int] = None, in_dtype: str = "bf16",
+                         decay_scale: float = 0.1, device="cuda") -> dict:
+    """The decode recipe drawn with torch on `device`: per-step tensors with a
+    leading `steps` axis, plus the initial fp32 state cache."""
+    torch = _torch()
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    slots = B if slots is None else slots
+    dt = torch.bfloat16 if in_dtype == "bf16" else torch.float32
+
+    def normal(*shape):
+        return torch.randn(*shape, generator=gen, device=device, dtype=torch.float32)
+
+    def unit(x):
+        return x / torch.linalg.vector_norm(x, dim=-1, keepdim=True).clamp_min(1e-30)
+
+    q = unit(normal(steps, B, H, K)).to(dt)
+    k = unit(normal(steps, B, H, K)).to(dt)
+    v = normal(steps, B, H, V).to(dt)
+    x = normal(steps, B, H, K)
+    log_alpha = (-torch.logaddexp(x, torch.zeros((), device=device)) * decay_scale).contiguous()
+    del x
+    beta = torch.sigmoid(normal(steps, B, H))
+    state = 0.02 * normal(slots, H, K, V)
+    return dict(q=q, k=k, v=v, log_alpha=log_alpha, beta=beta, state=state)
+
+
+def device_workload_inputs(name: str, device="cuda", steps: Optional[int] = None) -> dict:
+    """A named workload drawn on `device` (variable lengths still from numpy)."""
+    w = dict(WORKLOADS[name])
+    if w.pop("kind") == "decode":
+        if steps is not None:
+            w["steps"] = steps
+        return device_decode_inputs(device=device, **w)
+    lengths = w.pop("lengths")
+    n_seqs = w.pop("n_seqs", None)
+    lo, hi, total = w.pop("len_lo", None), w.pop("len_hi", None), w.pop("total", None)
+    if lengths is None:
+        lengths = varlen_lengths(np.random.default_rng(w["seed"]), n_seqs, lo, hi, total)
+    return device_prefill_inputs(lengths=lengths, device=device, **w)

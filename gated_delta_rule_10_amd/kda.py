@@ -1,0 +1,185 @@
+"""Python binding of libkda (include/kda.h): argument marshalling only.
+
+Every step of the operator runs in the HIP kernels of libkda.so. PyTorch is
+used for device memory and streams. If the library is not built, or a tensor
+is not on a GPU, the functions raise; there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
+
+KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
+KDA_F32, KDA_BF16 = 0, 1
+CHUNK_SIZE = 64
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    """A libkda entry point returned a status other than KDA_OK."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {kda_status_string(status)}")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libkda.so and declare its C signatures (no HIP call is made)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m gated_delta_rule_10_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.kda_abi_version.argtypes = []
+    lib.kda_abi_version.restype = ctypes.c_int
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_chunk_fwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
+    lib.kda_chunk_fwd_workspace_size.restype = sz
+    lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, ctypes.c_int,
+                                  ctypes.c_int, f32, P, P, P, i32, P, sz, P]
+    lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_decode_step.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                    ctypes.c_int, ctypes.c_int, f32, P]
+    lib.kda_decode_step.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def kda_abi_version() -> int:
+    return int(load_library().kda_abi_version())
+
+
+def kda_status_string(status: int) -> str:
+    return load_library().kda_status_string(int(status)).decode()
+
+
+def _code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return KDA_F32
+    if dt == torch.bfloat16:
+        return KDA_BF16
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def kda_chunk_fwd_workspace_size(N: int, T_total: int, H: int, d_k: int, d_v: int,
+                                 in_dtype: torch.dtype) -> int:
+    return int(load_library().kda_chunk_fwd_workspace_size(N, T_total, H, d_k, d_v,
+                                                           _code(in_dtype)))
+
+
+def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  log_alpha: torch.Tensor, beta: torch.Tensor, cu_seqlens: torch.Tensor,
+                  *, scale: float = 1.0, initial_state: Optional[torch.Tensor] = None,
+                  output_final_state: bool = True, final_state: Optional[torch.Tensor] = None,
+                  out_dtype: Optional[torch.dtype] = None, o: Optional[torch.Tensor] = None,
+                  chunk_size: int = CHUNK_SIZE, workspace: Optional[torch.Tensor] = None,
+                  stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunk prefill over packed sequences (see kda_chunk_fwd in include/kda.h).
+
+    q, k, log_alpha: [T, H, d_k]; v: [T, H, d_v]; beta: [T, H];
+    cu_seqlens: int32 [N+1] on the GPU; initial_state: fp32 [N, H, d_k, d_v] or None.
+    Returns (o [T, H, d_v], final_state [N, H, d_k, d_v] or None).
+    """
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta),
+                    ("cu_seqlens", cu_seqlens)):
+        _dev(t, name)
+    T, H, d_k = q.shape
+    d_v = v.shape[2]
+    N = cu_seqlens.shape[0] - 1
+    if k.shape != q.shape or log_alpha.shape != q.shape or v.shape[:2] != (T, H) \
+            or beta.shape != (T, H) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("inconsistent q/k/v/log_alpha/beta shapes or dtypes")
+    if log_alpha.dtype != torch.float32 or beta.dtype != torch.float32 \
+            or cu_seqlens.dtype != torch.int32:
+        raise ValueError("log_alpha and beta must be float32, cu_seqlens int32")
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((T, H, d_v), dtype=out_dtype, device=q.device)
+    elif o.shape != (T, H, d_v) or o.dtype != out_dtype:
+        raise ValueError("o has the wrong shape or dtype")
+    _dev(o, "o")
+    if initial_state is not None:
+        _dev(initial_state, "initial_state")
+        if initial_state.shape != (N, H, d_k, d_v) or initial_state.dtype != torch.float32:
+            raise ValueError("initial_state must be float32 [N, H, d_k, d_v]")
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, d_k, d_v), dtype=torch.float32, device=q.device)
+    if final_state is not None:
+        _dev(final_state, "final_state")
+        if final_state.shape != (N, H, d_k, d_v) or final_state.dtype != torch.float32:
+            raise ValueError("final_state must be float32 [N, H, d_k, d_v]")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                           _ptr(cu_seqlens), N, T, H, d_k, d_v, _code(q.dtype),
+                           _code(out_dtype), float(scale), _ptr(initial_state),
+                           _ptr(final_state), _ptr(o), int(chunk_size), _ptr(workspace),
+                           ws_bytes, _stream(stream))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_chunk_fwd")
+    return o, final_state
+
+
+def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    log_alpha: torch.Tensor, beta: torch.Tensor, state_cache: torch.Tensor,
+                    slot_idx: Optional[torch.Tensor] = None, *, scale: float = 1.0,
+                    out_dtype: Optional[torch.dtype] = None, o: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """One decode step, updating state_cache [slots, H, d_k, d_v] fp32 in place.
+
+    q, k, log_alpha: [B, H, d_k]; v: [B, H, d_v]; beta: [B, H];
+    slot_idx: int32 [B] on the GPU or None. Returns o [B, H, d_v].
+    """
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta),
+                    ("state_cache", state_cache)):
+        _dev(t, name)
+    B, H, d_k = q.shape
+    d_v = v.shape[2]
+    if k.shape != q.shape or log_alpha.shape != q.shape or v.shape[:2] != (B, H) \
+            or beta.shape != (B, H) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("inconsistent q/k/v/log_alpha/beta shapes or dtypes")
+    if state_cache.dtype != torch.float32 or state_cache.shape[1:] != (H, d_k, d_v):
+        raise ValueError("state_cache must be float32 [slots, H, d_k, d_v]")
+    if slot_idx is not None:
+        _dev(slot_idx, "slot_idx")
+        if slot_idx.dtype != torch.int32 or slot_idx.shape != (B,):
+            raise ValueError("slot_idx must be int32 [B]")
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((B, H, d_v), dtype=out_dtype, device=q.device)
+    _dev(o, "o")
+    st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                             _ptr(state_cache), _ptr(slot_idx), _ptr(o), B, H, d_k, d_v,
+                             state_cache.shape[0], _code(q.dtype), _code(out_dtype),
+                             float(scale), _stream(stream))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_decode_step")
+    return o

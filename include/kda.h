@@ -1,0 +1,153 @@
+/*
+ * kda.h -- C ABI of libkda: the Kimi Delta Attention (KDA) forward operator
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * KDA is the channel-wise gated delta rule. Per (sequence, head), with a
+ * d_k x d_v fp32 state S (row i = key channel i, column j = value channel j):
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = scale * S_t^T q_t
+ *
+ * with alpha_t = exp(log_alpha_t) one gate per key channel and beta_t one
+ * scalar per head. Sources: "Kimi Linear爆发背后的秘密：重新定义长上下文推理效率"
+ * (xugj520.cn), section "Kimi Delta Attention的技术内核" (the recurrence) and
+ * section "硬件效率的深度优化" (chunk-parallel inside a chunk, recurrent across
+ * chunks, WY representation, UT transform); the 2025 attention/MoE review
+ * (lanjinlin.com.cn), sections "GatedDeltaNet解读" (per-token loop: decay,
+ * correction against the decayed state, rank-1 write, read-out from the
+ * updated state, initial/final state of a sequence; state laid out as
+ * [heads, head_k_dim, head_v_dim]) and "KLA" (o_t = S_t^T q_t, Diag(alpha_t));
+ * "线性注意力机制Kimi Linear架构解析与优化实践" (coreui.cn), section 2.1 (alpha per key
+ * channel (B,H,D_k), beta per head (B,H,1)), section 2.2 (64-token chunks),
+ * section 3.2 (the recurrent state kept in one contiguous cache) and
+ * section 4.2 (the gate carried in log space).
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer argument is DEVICE memory on the current HIP device,
+ *    owned by the caller. The library never allocates, frees or
+ *    synchronises; all work is enqueued on `stream` and runs asynchronously.
+ *  - Every pointer must be 16-byte aligned; tensors are dense, row-major,
+ *    with the layouts given below (last dimension contiguous).
+ *  - Arguments are validated on the host before anything is enqueued. A
+ *    status other than KDA_OK means nothing was enqueued, except
+ *    KDA_ERR_HIP, which reports a failed kernel launch.
+ *  - Device-side contents are the caller's contract and are not checked:
+ *    cu_seqlens must be non-decreasing from 0 to T_total, log_alpha finite
+ *    and <= 0, slot indices distinct and in range. Stability of the
+ *    recurrence needs ||k_t|| <= 1 and beta_t in [0, 2].
+ *  - Functions hold no global mutable state and are re-entrant; calls on
+ *    different streams that write the same memory race.
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1, /* NULL, misaligned pointer or out-of-range size */
+    KDA_ERR_UNSUPPORTED = 2, /* valid but not implemented: head dims, chunk size, dtype pair */
+    KDA_ERR_WORKSPACE = 3,   /* workspace smaller than kda_chunk_fwd_workspace_size() */
+    KDA_ERR_HIP = 4          /* a HIP launch failed; see hipGetLastError() */
+} kda_status_t;
+
+typedef enum {
+    KDA_F32 = 0,  /* IEEE binary32 */
+    KDA_BF16 = 1  /* bfloat16; outputs are rounded to nearest even */
+} kda_dtype_t;
+
+/* KDA_ABI_VERSION of the loaded library. */
+int kda_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. Never NULL. */
+const char *kda_status_string(kda_status_t status);
+
+/*
+ * Bytes of device workspace kda_chunk_fwd needs for these sizes; 0 means the
+ * call may pass workspace = NULL. Pure function of its arguments.
+ */
+size_t kda_chunk_fwd_workspace_size(int32_t N, int32_t T_total, int32_t H,
+                                    int32_t d_k, int32_t d_v,
+                                    kda_dtype_t in_dtype);
+
+/*
+ * Chunkwise-parallel KDA prefill over N packed variable-length sequences.
+ *
+ * Sequence n covers tokens [cu_seqlens[n], cu_seqlens[n+1]) of the packed
+ * token axis. Each sequence starts from initial_state[n] (zeros if
+ * initial_state is NULL) and is cut into 64-token chunks from its own first
+ * token; the last chunk may be partial. The result is the recurrence above
+ * evaluated exactly up to floating-point rounding: the chunk size is not
+ * part of the result.
+ *
+ *   q, k        [T_total, H, d_k]   in_dtype
+ *   v           [T_total, H, d_v]   in_dtype
+ *   log_alpha   [T_total, H, d_k]   fp32, natural-log channel gate, <= 0
+ *   beta        [T_total, H]        fp32
+ *   cu_seqlens  [N + 1]             int32, device memory
+ *   initial_state [N, H, d_k, d_v]  fp32, or NULL for zeros
+ *   final_state   [N, H, d_k, d_v]  fp32 output, or NULL (not written);
+ *                                   may be the same pointer as initial_state
+ *   o           [T_total, H, d_v]   out_dtype output
+ *   scale       multiplies o only (not the state); 1.0 gives o_t = S_t^T q_t
+ *   chunk_size  must be 64
+ *   workspace   device scratch of workspace_bytes (may be NULL if the size
+ *               query returns 0)
+ *
+ * Sizes: N >= 1, H >= 1, T_total >= 0, d_k and d_v in {64, 128}.
+ * dtype pairs: (F32 in, F32 out), (BF16 in, BF16 out), (BF16 in, F32 out).
+ * Internal arithmetic: fp32 state and accumulation; the state is fp32 at
+ * every chunk boundary.
+ * A sequence of length 0 leaves final_state[n] = initial_state[n] (or 0).
+ */
+kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v,
+                           const float *log_alpha, const float *beta,
+                           const int32_t *cu_seqlens, int32_t N,
+                           int32_t T_total, int32_t H, int32_t d_k,
+                           int32_t d_v, kda_dtype_t in_dtype,
+                           kda_dtype_t out_dtype, float scale,
+                           const float *initial_state, float *final_state,
+                           void *o, int32_t chunk_size, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * One recurrent decode step for B independent sequences, updating an fp32
+ * state cache in place (one token per sequence).
+ *
+ *   q, k        [B, H, d_k]   in_dtype
+ *   v           [B, H, d_v]   in_dtype
+ *   log_alpha   [B, H, d_k]   fp32
+ *   beta        [B, H]        fp32
+ *   state_cache [num_slots, H, d_k, d_v] fp32, read and written in place
+ *   slot_idx    [B] int32 device array of distinct slots in [0, num_slots),
+ *               or NULL for slot b = b (then B <= num_slots)
+ *   o           [B, H, d_v]   out_dtype output
+ *
+ * Per (b, h): S' = Diag(exp(log_alpha)) S; u = beta (v - S'^T k);
+ * S = S' + k u^T; o = scale * S^T q.
+ * Sizes: B >= 1, H >= 1, num_slots >= 1, d_k and d_v in {64, 128}.
+ * dtype pairs as for kda_chunk_fwd.
+ */
+kda_status_t kda_decode_step(const void *q, const void *k, const void *v,
+                             const float *log_alpha, const float *beta,
+                             float *state_cache, const int32_t *slot_idx,
+                             void *o, int32_t B, int32_t H, int32_t d_k,
+                             int32_t d_v, int32_t num_slots,
+                             kda_dtype_t in_dtype, kda_dtype_t out_dtype,
+                             float scale, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

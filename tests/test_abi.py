@@ -1,0 +1,112 @@
+"""CPU tests of the C ABI: the library loads, exports every symbol that
+include/kda.h declares, and rejects invalid arguments on the host before any
+HIP call (so these run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_10_amd import kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+A = 0x10000  # a 16-byte aligned stand-in address; never dereferenced on the host
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.LIB_PATH):
+        pytest.skip("libkda.so not built")
+    return kda.load_library()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted([
+        "kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_size",
+        "kda_chunk_fwd", "kda_decode_step"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert kda.kda_abi_version() == 1
+    for s in range(5):
+        assert kda.kda_status_string(s).startswith("KDA_")
+    assert "unknown" in kda.kda_status_string(99)
+
+
+def _prefill(lib, **over):
+    args = dict(q=A, k=A, v=A, g=A, b=A, cu=A, N=2, T=100, H=4, dk=128, dv=128,
+                din=kda.KDA_BF16, dout=kda.KDA_BF16, scale=1.0, s0=None, sT=None, o=A,
+                chunk=64, ws=None, wsb=0)
+    args.update(over)
+    return lib.kda_chunk_fwd(args["q"], args["k"], args["v"], args["g"], args["b"],
+                             args["cu"], args["N"], args["T"], args["H"], args["dk"],
+                             args["dv"], args["din"], args["dout"], args["scale"],
+                             args["s0"], args["sT"], args["o"], args["chunk"], args["ws"],
+                             args["wsb"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(cu=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(o=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(v=A + 8), kda.KDA_ERR_INVALID_ARG),
+    (dict(s0=A + 4), kda.KDA_ERR_INVALID_ARG),
+    (dict(N=0), kda.KDA_ERR_INVALID_ARG),
+    (dict(H=0), kda.KDA_ERR_INVALID_ARG),
+    (dict(T=-1), kda.KDA_ERR_INVALID_ARG),
+    (dict(din=7), kda.KDA_ERR_INVALID_ARG),
+    (dict(dk=96), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dv=256), kda.KDA_ERR_UNSUPPORTED),
+    (dict(chunk=128), kda.KDA_ERR_UNSUPPORTED),
+    (dict(din=kda.KDA_F32, dout=kda.KDA_BF16), kda.KDA_ERR_UNSUPPORTED),
+])
+def test_chunk_fwd_rejects(lib, over, status):
+    assert _prefill(lib, **over) == status
+
+
+def test_workspace_query(lib):
+    assert kda.kda_chunk_fwd_workspace_size(16, 524288, 32, 128, 128, __import__("torch").bfloat16) == 0
+
+
+def _decode(lib, **over):
+    args = dict(q=A, k=A, v=A, g=A, b=A, st=A, si=None, o=A, B=4, H=2, dk=128, dv=128,
+                slots=4, din=kda.KDA_BF16, dout=kda.KDA_BF16, scale=1.0)
+    args.update(over)
+    return lib.kda_decode_step(args["q"], args["k"], args["v"], args["g"], args["b"],
+                               args["st"], args["si"], args["o"], args["B"], args["H"],
+                               args["dk"], args["dv"], args["slots"], args["din"],
+                               args["dout"], args["scale"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(st=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(k=A + 2), kda.KDA_ERR_INVALID_ARG),
+    (dict(B=0), kda.KDA_ERR_INVALID_ARG),
+    (dict(B=5), kda.KDA_ERR_INVALID_ARG),  # identity slots need B <= num_slots
+    (dict(slots=0), kda.KDA_ERR_INVALID_ARG),
+    (dict(dk=32), kda.KDA_ERR_UNSUPPORTED),
+    (dict(din=kda.KDA_F32, dout=kda.KDA_BF16), kda.KDA_ERR_UNSUPPORTED),
+])
+def test_decode_rejects(lib, over, status):
+    assert _decode(lib, **over) == status
+
+
+def test_binding_refuses_host_tensors(lib):
+    import torch
+    x = torch.zeros((4, 2, 64))
+    with pytest.raises(ValueError):
+        kda.kda_chunk_fwd(x, x, x, x, torch.zeros((4, 2)), torch.zeros(2, dtype=torch.int32))
