@@ -53,8 +53,10 @@ const char *kda_status_string(kda_status_t s) {
 
 size_t kda_chunk_fwd_workspace_size(int32_t N, int32_t T_total, int32_t H, int32_t d_k,
                                     int32_t d_v, kda_dtype_t in_dtype) {
-    (void)N; (void)T_total; (void)H; (void)d_k; (void)d_v; (void)in_dtype;
-    return 0;  // every kernel keeps its intermediates on chip
+    if (N < 1 || H < 1 || T_total < 0 || !head_dim_ok(d_k) || !head_dim_ok(d_v)) return 0;
+    // the bf16 path stages every chunk's state-independent operands in the workspace
+    if (in_dtype == KDA_BF16 && !force_valu()) return kda::prefill_mfma_workspace(N, T_total, H, d_k, d_v);
+    return 0;
 }
 
 kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
@@ -87,6 +89,7 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const fl
     a.s0 = initial_state; a.sT = final_state; a.o = o;
     a.N = N; a.T = T_total; a.H = H; a.K = d_k; a.V = d_v; a.scale = scale;
     a.in_dtype = in_dtype; a.out_dtype = out_dtype;
+    a.ws = workspace; a.ws_bytes = workspace_bytes;
     hipError_t e;
     if (in_dtype == KDA_BF16 && !force_valu())
         e = kda::launch_prefill_mfma(a, stream);

@@ -21,6 +21,8 @@ struct PrefillArgs {
     int32_t N, T, H, K, V;
     float scale;
     kda_dtype_t in_dtype, out_dtype;
+    void *ws;                    // caller workspace (matrix-core path)
+    size_t ws_bytes;
 };
 
 struct DecodeArgs {
@@ -40,5 +42,8 @@ struct DecodeArgs {
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_prefill_valu(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream);
+
+// Workspace bytes of the matrix-core prefill (0 for d_k/d_v it cannot run).
+size_t prefill_mfma_workspace(int32_t N, int32_t T, int32_t H, int32_t K, int32_t V);
 
 }  // namespace kda

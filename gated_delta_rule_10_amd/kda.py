@@ -136,6 +136,10 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         _dev(final_state, "final_state")
         if final_state.shape != (N, H, d_k, d_v) or final_state.dtype != torch.float32:
             raise ValueError("final_state must be float32 [N, H, d_k, d_v]")
+    if workspace is None:
+        need = int(lib.kda_chunk_fwd_workspace_size(N, T, H, d_k, d_v, _code(q.dtype)))
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
                            _ptr(cu_seqlens), N, T, H, d_k, d_v, _code(q.dtype),
