@@ -72,9 +72,13 @@ __device__ __forceinline__ float col_scale(float m, float &inv) {
     return __uint_as_float(static_cast<uint32_t>(127 - 14 + e) << 23);
 }
 
+// max over the four lanes l, l^16, l^32, l^48 (one column of an MFMA result):
+// a lane swap of a register with itself pairs every lane with its partner
 __device__ __forceinline__ float col_max(float m) {
-    m = fmaxf(m, __shfl_xor(m, 16));
-    return fmaxf(m, __shfl_xor(m, 32));
+    const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    m = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+    const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    return fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
 }
 
 // Per (chunk, head) record in the workspace; every fragment is 64 lanes x 16 B.
@@ -97,6 +101,13 @@ __device__ __forceinline__ int tri(int i, int ks) { return i < 2 ? i : 2 * i - 2
 __device__ __forceinline__ int vblk(int i, int j) { return (j == 0 ? 0 : j == 1 ? 4 : j == 2 ? 7 : 9) + i - j; }
 
 constexpr size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// chunk capacity: an upper bound of sum_n ceil(len_n / 64); records are stored
+// head-major, record (chunk c, head h) at index h * capacity + c, so one head's
+// consecutive chunks are adjacent in memory
+__host__ __device__ __forceinline__ size_t a_nc(const PrefillArgs &a) {
+    return static_cast<size_t>((a.T + kC - 1) / kC) + a.N;
+}
 
 // ---------------------------------------------------------------------------
 // chunk offsets: off[n] = sum_{m<n} ceil(len_m / 64), off[N] = total chunks
@@ -165,7 +176,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a, const int32_t 
     const int n = lo;
     const int t0 = a.cu_seqlens[n] + (c - off[n]) * kC;
     const int nt = min(kC, a.cu_seqlens[n + 1] - t0);
-    char *rec = recs + (static_cast<size_t>(c) * H + h) * R::BYTES;
+    char *rec = recs + (static_cast<size_t>(h) * a_nc(a) + c) * R::BYTES;
 
     const int tid = threadIdx.x, l = tid & 63, r = l & 15, g = l >> 4;
     // wave index as a scalar: branches on it must be real jumps, because a
@@ -397,21 +408,33 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a, const int32_t 
 }
 
 // ---------------------------------------------------------------------------
-// scan: sequential pass over the chunks of one (sequence, head, 16 columns)
+// scan: sequential pass over the chunks of one (sequence, head, 16 value columns)
 template <int K>
 struct Frags {
-    static constexpr int NCB = K / 32;
+    float4 v;              // this thread's 4 columns of one token of V (staged through LDS)
+    float bet;             // beta of token `tid` (threads < 64)
     half8 kexp[4], qg[4];  // this wave's channel block, all four token row blocks
     half8 kgt[2][2];       // this wave's two channel tiles x two token steps
-    half8 t[6];
+    half8 t[2];            // T fragments w and w + 4 (w + 4 exists for w < 2), staged through LDS
     half8 p[2];            // this wave's output row block
     f4 gam[2];
 };
 
-template <int K>
-__device__ __forceinline__ void load_frags(Frags<K> &f, const char *rec, int w, int l, int g) {
+// Loads every operand of chunk c (clamped to the last chunk, so the loads are
+// unconditional). V and beta come first: they are consumed earliest.
+template <int K, int V>
+__device__ __forceinline__ void load_frags(Frags<K> &f, const char *recs, size_t nc, int c, int clast, int H, int h,
+                                           const bf16_t *vg, int tbeg, int tend, int cbeg, int j0, int tid,
+                                           int w, int l, int g) {
     using R = Rec<K>;
     constexpr int NCB = K / 32;
+    c = min(c, clast);
+    const char *rec = recs + (static_cast<size_t>(h) * nc + c) * R::BYTES;
+    const int stok = tid >> 2, sc4 = (tid & 3) * 4;
+    const int tok = tbeg + (c - cbeg) * kC + stok;
+    const float4 vv = io<bf16_t>::load4(vg + (static_cast<size_t>(min(tok, tend - 1)) * H + h) * V + j0 + sc4);
+    f.v = tok < tend ? vv : make_float4(0.f, 0.f, 0.f, 0.f);
+    f.bet = reinterpret_cast<const float *>(rec + R::BET)[tid & 63];
     if (w < NCB) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -426,20 +449,153 @@ __device__ __forceinline__ void load_frags(Frags<K> &f, const char *rec, int w, 
             f.gam[tt] = *reinterpret_cast<const f4 *>(rec + R::GAM + (16 * (2 * w + tt) + 4 * g) * 4);
         }
     }
-#pragma unroll
-    for (int i = 0; i < 6; ++i) f.t[i] = *reinterpret_cast<const half8 *>(rec + R::TM + (i * 64 + l) * 16);
+    f.t[0] = *reinterpret_cast<const half8 *>(rec + R::TM + (w * 64 + l) * 16);
+    f.t[1] = *reinterpret_cast<const half8 *>(rec + R::TM + ((w < 2 ? w + 4 : w) * 64 + l) * 16);
     f.p[0] = *reinterpret_cast<const half8 *>(rec + R::PM + (tri(w, 0) * 64 + l) * 16);
-    f.p[1] = w >= 2 ? *reinterpret_cast<const half8 *>(rec + R::PM + (tri(w, 1) * 64 + l) * 16) : f.p[0];
+    f.p[1] = *reinterpret_cast<const half8 *>(rec + R::PM + (tri(w, w >= 2 ? 1 : 0) * 64 + l) * 16);
+}
+
+template <int K, int V, typename TOut>
+struct ScanSmem {
+    static constexpr int NCB = K / 32;
+    f4 partX[2][NCB][4][64];  // (K.e^G) S_w / sig_w per wave w (channel block)
+    f4 partO[2][NCB][4][64];  // (Q.e^G) S_w / sig_w
+    float sig[2][NCB][64];    // sig_w of the lane's column
+    float vT[2][16][kC + 4];
+    float bet[2][kC];
+    half8 t[2][6][64];  // T fragments of the current / next chunk
+};
+
+// Stage chunk data that every wave needs (V transposed, beta) into LDS buffer b.
+template <int K, int V, typename TOut>
+__device__ __forceinline__ void stage(ScanSmem<K, V, TOut> &sm, int b, const Frags<K> &f, int tid) {
+    const int stok = tid >> 2, sc4 = (tid & 3) * 4;
+    sm.vT[b][sc4 + 0][stok] = f.v.x;
+    sm.vT[b][sc4 + 1][stok] = f.v.y;
+    sm.vT[b][sc4 + 2][stok] = f.v.z;
+    sm.vT[b][sc4 + 3][stok] = f.v.w;
+    if (tid < kC) sm.bet[b][tid] = f.bet;
+    const int w = tid >> 6, l = tid & 63;
+    sm.t[b][w][l] = f.t[0];
+    if (w < 2) sm.t[b][w + 4][l] = f.t[1];
+}
+
+// One chunk of the state pass; `f` holds chunk c's operands, V/beta already
+// staged in LDS buffer `buf`. Ends by staging `fn` (chunk c + 1) into buf ^ 1.
+template <int K, int V, typename TOut>
+__device__ __forceinline__ void scan_chunk(ScanSmem<K, V, TOut> &sm, const Frags<K> &f, const Frags<K> &fn,
+                                           f4 (&S)[2], int buf, bool more, int t0, int nt, int H, int h,
+                                           int j0, TOut *og, float scale, int tid, int w, int l, int r,
+                                           int g) {
+    constexpr int NCB = K / 32;
+    const bool hasS = w < NCB;
+    // (a) partial products with this wave's channel block of the state
+    if (hasS) {
+        float m = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(fabsf(S[0][e]), fabsf(S[1][e])));
+        float inv;
+        const float sig = col_scale(col_max(m), inv);
+        half8 sf;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sf[e] = static_cast<_Float16>(S[0][e] * inv);
+            sf[4 + e] = static_cast<_Float16>(S[1][e] * inv);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sm.partX[buf][w][i][l] = mfma(f.kexp[i], sf, zero4());
+            sm.partO[buf][w][i][l] = mfma(f.qg[i], sf, zero4());
+        }
+        sm.sig[buf][w][l] = sig;
+    }
+    __syncthreads();
+
+    // (b) X = Diag(beta)(V - (K.e^G) S) for all 64 tokens, column j0 + r
+    f4 X[4];
+    float mx = 0.f;
+    float sw[NCB];
+#pragma unroll
+    for (int ww = 0; ww < NCB; ++ww) sw[ww] = sm.sig[buf][ww][l];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f4 ks = sm.partX[buf][0][i][l] * sw[0];
+#pragma unroll
+        for (int ww = 1; ww < NCB; ++ww) ks += sm.partX[buf][ww][i][l] * sw[ww];
+        const f4 vv = *reinterpret_cast<const f4 *>(&sm.vT[buf][r][16 * i + 4 * g]);
+        const f4 bb = *reinterpret_cast<const f4 *>(&sm.bet[buf][16 * i + 4 * g]);
+        X[i] = bb * (vv - ks);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(X[i][e]));
+    }
+    float invx;
+    const float sigx = col_scale(col_max(mx), invx);
+    half8 xf[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            xf[ks][e] = static_cast<_Float16>(X[2 * ks][e] * invx);
+            xf[ks][4 + e] = static_cast<_Float16>(X[2 * ks + 1][e] * invx);
+        }
+
+    // (c) U' = T X
+    f4 U[4];
+    U[0] = mfma(sm.t[buf][0][l], xf[0], zero4());
+    U[1] = mfma(sm.t[buf][1][l], xf[0], zero4());
+    U[2] = mfma(sm.t[buf][3][l], xf[1], mfma(sm.t[buf][2][l], xf[0], zero4()));
+    U[3] = mfma(sm.t[buf][5][l], xf[1], mfma(sm.t[buf][4][l], xf[0], zero4()));
+    // U holds U' / sigx; pick U' / sigu with the column maximum of U' in [2^14, 2^15)
+    float mu = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mu = fmaxf(mu, fabsf(U[i][e]));
+    float invu;
+    const float sigu = col_scale(col_max(mu) * sigx, invu);
+    const float ru = sigx * invu;
+    half8 uf[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            uf[ks][e] = static_cast<_Float16>(U[2 * ks][e] * ru);
+            uf[ks][4 + e] = static_cast<_Float16>(U[2 * ks + 1][e] * ru);
+        }
+
+    // (d) S <- Diag(e^{G_n}) S + (K.e^{G_n-G})^T U'
+    if (hasS) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            f4 acc = S[tt] * f.gam[tt] * invu;
+            acc = mfma(f.kgt[tt][0], uf[0], acc);
+            acc = mfma(f.kgt[tt][1], uf[1], acc);
+            S[tt] = acc * sigu;
+        }
+    }
+
+    // (e) O rows of token block w = (Q.e^G) S + P U'
+    {
+        f4 ov = sm.partO[buf][0][w][l] * sw[0];
+#pragma unroll
+        for (int ww = 1; ww < NCB; ++ww) ov += sm.partO[buf][ww][w][l] * sw[ww];
+        f4 pu = mfma(f.p[0], uf[0], zero4());
+        if (w >= 2) pu = mfma(f.p[1], uf[1], pu);
+        ov = (ov + pu * sigu) * scale;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int tok = 16 * w + 4 * g + e;
+            if (tok < nt) io<TOut>::store(og + (static_cast<size_t>(t0 + tok) * H + h) * V + j0 + r, ov[e]);
+        }
+    }
+    // the buffer of the next chunk was last read before this chunk's barrier
+    if (more) stage<K, V, TOut>(sm, buf ^ 1, fn, tid);
 }
 
 template <int K, int V, typename TOut>
 __global__ __launch_bounds__(256) void scan_kernel(PrefillArgs a, const int32_t *off, const char *recs) {
     constexpr int NCB = K / 32, NV = V / 16;
-    using R = Rec<K>;
-    __shared__ f4 partX[2][NCB][4][64];
-    __shared__ f4 partO[2][NCB][4][64];
-    __shared__ float vT[2][16][kC + 4];
-    __shared__ float bet[2][kC];
+    __shared__ ScanSmem<K, V, TOut> sm;
 
     // blockIdx -> (unit, value tile) with the NV tiles of a unit on one XCD
     const int bid = blockIdx.x, xcd = bid & 7, q8 = bid >> 3;
@@ -448,8 +604,6 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillArgs a, const int32_t 
     const int n = unit / a.H, h = unit - (unit / a.H) * a.H, j0 = vt * 16;
     const int H = a.H;
     const int tid = threadIdx.x, l = tid & 63, r = l & 15, g = l >> 4;
-    // wave index as a scalar: branches on it must be real jumps, because a
-    // matrix instruction inside an EXEC-masked block still writes its result
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool hasS = w < NCB;
     const size_t sbase = (static_cast<size_t>(n) * H + h) * static_cast<size_t>(K) * V;
@@ -464,137 +618,27 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillArgs a, const int32_t 
     }
     const int cbeg = off[n], cend = off[n + 1];
     const int tbeg = a.cu_seqlens[n], tend = a.cu_seqlens[n + 1];
+    const size_t nc = a_nc(a);
     const bf16_t *vg = static_cast<const bf16_t *>(a.v);
     TOut *og = static_cast<TOut *>(a.o);
 
-    // staging of V (transposed) and beta for one chunk: thread -> (token, 4 columns)
-    const int stok = tid >> 2, sc4 = (tid & 3) * 4;
-    auto load_v = [&](int c) -> float4 {
-        const int t0 = tbeg + (c - cbeg) * kC;
-        if (c < cend && t0 + stok < tend)
-            return io<bf16_t>::load4(vg + (static_cast<size_t>(t0 + stok) * H + h) * V + j0 + sc4);
-        return make_float4(0.f, 0.f, 0.f, 0.f);
-    };
-    auto stage = [&](int b, float4 vv, const char *rec) {
-        vT[b][sc4 + 0][stok] = vv.x; vT[b][sc4 + 1][stok] = vv.y;
-        vT[b][sc4 + 2][stok] = vv.z; vT[b][sc4 + 3][stok] = vv.w;
-        if (tid < kC) bet[b][tid] = reinterpret_cast<const float *>(rec + R::BET)[tid];
-    };
-
-    Frags<K> cur, nxt;
     if (cbeg < cend) {
-        const char *rec0 = recs + (static_cast<size_t>(cbeg) * H + h) * R::BYTES;
-        load_frags<K>(cur, rec0, w, l, g);
-        stage(0, load_v(cbeg), rec0);
-    }
-    __syncthreads();
-    int buf = 0;
-    for (int c = cbeg; c < cend; ++c, buf ^= 1) {
-        const int t0 = tbeg + (c - cbeg) * kC;
-        const int nt = min(kC, tend - t0);
-        const bool more = c + 1 < cend;
-        const char *recn = recs + (static_cast<size_t>(more ? c + 1 : c) * H + h) * R::BYTES;
-        load_frags<K>(nxt, recn, w, l, g);  // prefetch the next chunk
-        const float4 vnext = load_v(c + 1);
-
-        // (a) partial products with this wave's channel block of the state
-        if (hasS) {
-            float m = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(fabsf(S[0][e]), fabsf(S[1][e])));
-            float inv;
-            const float sig = col_scale(col_max(m), inv);
-            half8 sf;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sf[e] = static_cast<_Float16>(S[0][e] * inv);
-                sf[4 + e] = static_cast<_Float16>(S[1][e] * inv);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                partX[buf][w][i][l] = mfma(cur.kexp[i], sf, zero4()) * sig;
-                partO[buf][w][i][l] = mfma(cur.qg[i], sf, zero4()) * sig;
-            }
-        }
+        // operands of the next chunk are loaded while the current one is processed;
+        // the copy at the top of the loop waits for loads issued one chunk earlier
+        Frags<K> nx;
+        const int clast = cend - 1;
+        load_frags<K, V>(nx, recs, nc, cbeg, clast, H, h, vg, tbeg, tend, cbeg, j0, tid, w, l, g);
+        stage<K, V, TOut>(sm, 0, nx, tid);
         __syncthreads();
-
-        // (b) X = Diag(beta)(V - (K.e^G) S) for all 64 tokens, column j0 + r
-        f4 X[4];
-        float mx = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f4 ks = partX[buf][0][i][l];
-#pragma unroll
-            for (int ww = 1; ww < NCB; ++ww) ks += partX[buf][ww][i][l];
-            const f4 vv = *reinterpret_cast<const f4 *>(&vT[buf][r][16 * i + 4 * g]);
-            const f4 bb = *reinterpret_cast<const f4 *>(&bet[buf][16 * i + 4 * g]);
-            X[i] = bb * (vv - ks);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(X[i][e]));
+        int buf = 0;
+        for (int c = cbeg; c < cend; ++c, buf ^= 1) {
+            const Frags<K> cu = nx;
+            load_frags<K, V>(nx, recs, nc, c + 1, clast, H, h, vg, tbeg, tend, cbeg, j0, tid, w, l, g);
+            __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the chunk's work
+            const int t0 = tbeg + (c - cbeg) * kC;
+            scan_chunk<K, V, TOut>(sm, cu, nx, S, buf, c + 1 < cend, t0, min(kC, tend - t0), H, h, j0, og,
+                                   a.scale, tid, w, l, r, g);
         }
-        float invx;
-        const float sigx = col_scale(col_max(mx), invx);
-        half8 xf[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                xf[ks][e] = static_cast<_Float16>(X[2 * ks][e] * invx);
-                xf[ks][4 + e] = static_cast<_Float16>(X[2 * ks + 1][e] * invx);
-            }
-
-        // (c) U' = T X
-        f4 U[4];
-        U[0] = mfma(cur.t[0], xf[0], zero4());
-        U[1] = mfma(cur.t[1], xf[0], zero4());
-        U[2] = mfma(cur.t[3], xf[1], mfma(cur.t[2], xf[0], zero4()));
-        U[3] = mfma(cur.t[5], xf[1], mfma(cur.t[4], xf[0], zero4()));
-        float mu = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            U[i] *= sigx;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) mu = fmaxf(mu, fabsf(U[i][e]));
-        }
-        float invu;
-        const float sigu = col_scale(col_max(mu), invu);
-        half8 uf[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                uf[ks][e] = static_cast<_Float16>(U[2 * ks][e] * invu);
-                uf[ks][4 + e] = static_cast<_Float16>(U[2 * ks + 1][e] * invu);
-            }
-
-        // (d) S <- Diag(e^{G_n}) S + (K.e^{G_n-G})^T U'
-        if (hasS) {
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                f4 acc = S[tt] * cur.gam[tt] * invu;
-                acc = mfma(cur.kgt[tt][0], uf[0], acc);
-                acc = mfma(cur.kgt[tt][1], uf[1], acc);
-                S[tt] = acc * sigu;
-            }
-        }
-
-        // (e) O rows of token block w = (Q.e^G) S + P U'
-        {
-            f4 ov = partO[buf][0][w][l];
-#pragma unroll
-            for (int ww = 1; ww < NCB; ++ww) ov += partO[buf][ww][w][l];
-            f4 pu = mfma(cur.p[0], uf[0], zero4());
-            if (w >= 2) pu = mfma(cur.p[1], uf[1], pu);
-            ov = (ov + pu * sigu) * a.scale;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int tok = 16 * w + 4 * g + e;
-                if (tok < nt) io<TOut>::store(og + (static_cast<size_t>(t0 + tok) * H + h) * V + j0 + r, ov[e]);
-            }
-        }
-        // publish the next chunk's V and beta (its buffer was last read before this chunk's barrier)
-        if (more) stage(buf ^ 1, vnext, recn);
-        cur = nxt;
     }
     if (hasS && a.sT) {
 #pragma unroll
@@ -608,7 +652,7 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillArgs a, const int32_t 
 template <int K, int V>
 hipError_t launch_kv(const PrefillArgs &a, hipStream_t st) {
     using R = Rec<K>;
-    const size_t nc_max = static_cast<size_t>((a.T + kC - 1) / kC) + a.N;
+    const size_t nc_max = a_nc(a);
     int32_t *off = static_cast<int32_t *>(a.ws);
     char *recs = static_cast<char *>(a.ws) + align256(static_cast<size_t>(a.N + 1) * 4);
     hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(256), 0, st, a.cu_seqlens, a.N, off);
