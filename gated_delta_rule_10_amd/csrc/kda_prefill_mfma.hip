@@ -411,49 +411,72 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a, const int32_t 
 // scan: sequential pass over the chunks of one (sequence, head, 16 value columns)
 template <int K>
 struct Frags {
-    float4 v;              // this thread's 4 columns of one token of V (staged through LDS)
-    float bet;             // beta of token `tid` (threads < 64)
+    float4 v;              // this thread's 4 columns of one token of V        (staged to LDS)
+    float aux;             // beta (threads 0..63) or e^{G_n} (threads 64..191) (staged to LDS)
+    half8 t[2];            // T fragments w and w + 4 (w + 4 exists for w < 2)  (staged to LDS)
     half8 kexp[4], qg[4];  // this wave's channel block, all four token row blocks
     half8 kgt[2][2];       // this wave's two channel tiles x two token steps
-    half8 t[2];            // T fragments w and w + 4 (w + 4 exists for w < 2), staged through LDS
     half8 p[2];            // this wave's output row block
-    f4 gam[2];
 };
 
-// Loads every operand of chunk c (clamped to the last chunk, so the loads are
-// unconditional). V and beta come first: they are consumed earliest.
+// Operand loads of chunk c (clamped to the last chunk, so they are unconditional),
+// in four parts that the chunk loop spreads over the previous chunk's work: one
+// burst of all of them saturates the CU's vector memory pipeline.
 template <int K, int V>
-__device__ __forceinline__ void load_frags(Frags<K> &f, const char *recs, size_t nc, int c, int clast, int H, int h,
-                                           const bf16_t *vg, int tbeg, int tend, int cbeg, int j0, int tid,
-                                           int w, int l, int g) {
-    using R = Rec<K>;
-    constexpr int NCB = K / 32;
-    c = min(c, clast);
-    const char *rec = recs + (static_cast<size_t>(h) * nc + c) * R::BYTES;
-    const int stok = tid >> 2, sc4 = (tid & 3) * 4;
-    const int tok = tbeg + (c - cbeg) * kC + stok;
-    const float4 vv = io<bf16_t>::load4(vg + (static_cast<size_t>(min(tok, tend - 1)) * H + h) * V + j0 + sc4);
-    f.v = tok < tend ? vv : make_float4(0.f, 0.f, 0.f, 0.f);
-    f.bet = reinterpret_cast<const float *>(rec + R::BET)[tid & 63];
-    if (w < NCB) {
+struct FragLoader {
+    const char *rec;
+    const bf16_t *vrow;
+    bool vok;
+
+    __device__ __forceinline__ FragLoader(const char *recs, size_t nc, int c, int clast, int H, int h,
+                                          const bf16_t *vg, int tbeg, int tend, int cbeg, int j0, int tid) {
+        c = min(c, clast);
+        rec = recs + (static_cast<size_t>(h) * nc + c) * Rec<K>::BYTES;
+        const int tok = tbeg + (c - cbeg) * kC + (tid >> 2);
+        vok = tok < tend;
+        vrow = vg + (static_cast<size_t>(min(tok, tend - 1)) * H + h) * V + j0 + (tid & 3) * 4;
+    }
+    __device__ __forceinline__ void part0(Frags<K> &f, int tid, int w, int l) const {
+        using R = Rec<K>;
+        const float4 vv = io<bf16_t>::load4(vrow);
+        f.v = vok ? vv : make_float4(0.f, 0.f, 0.f, 0.f);
+        if (tid < 64) f.aux = reinterpret_cast<const float *>(rec + R::BET)[tid];
+        else if (tid < 64 + K) f.aux = reinterpret_cast<const float *>(rec + R::GAM)[tid - 64];
+        f.t[0] = *reinterpret_cast<const half8 *>(rec + R::TM + (w * 64 + l) * 16);
+        if (w < 2) f.t[1] = *reinterpret_cast<const half8 *>(rec + R::TM + ((w + 4) * 64 + l) * 16);
+    }
+    __device__ __forceinline__ void part1(Frags<K> &f, int w, int l) const {
+        using R = Rec<K>;
+        constexpr int NCB = K / 32;
+        if (w < NCB) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f.kexp[i] = *reinterpret_cast<const half8 *>(rec + R::KEXP + ((i * NCB + w) * 64 + l) * 16);
-            f.qg[i] = *reinterpret_cast<const half8 *>(rec + R::QG + ((i * NCB + w) * 64 + l) * 16);
-        }
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                f.kgt[tt][ks] = *reinterpret_cast<const half8 *>(rec + R::KGT + (((2 * w + tt) * 2 + ks) * 64 + l) * 16);
-            f.gam[tt] = *reinterpret_cast<const f4 *>(rec + R::GAM + (16 * (2 * w + tt) + 4 * g) * 4);
+            for (int i = 0; i < 4; ++i)
+                f.kexp[i] = *reinterpret_cast<const half8 *>(rec + R::KEXP + ((i * NCB + w) * 64 + l) * 16);
         }
     }
-    f.t[0] = *reinterpret_cast<const half8 *>(rec + R::TM + (w * 64 + l) * 16);
-    f.t[1] = *reinterpret_cast<const half8 *>(rec + R::TM + ((w < 2 ? w + 4 : w) * 64 + l) * 16);
-    f.p[0] = *reinterpret_cast<const half8 *>(rec + R::PM + (tri(w, 0) * 64 + l) * 16);
-    f.p[1] = *reinterpret_cast<const half8 *>(rec + R::PM + (tri(w, w >= 2 ? 1 : 0) * 64 + l) * 16);
-}
+    __device__ __forceinline__ void part2(Frags<K> &f, int w, int l) const {
+        using R = Rec<K>;
+        constexpr int NCB = K / 32;
+        if (w < NCB) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                f.qg[i] = *reinterpret_cast<const half8 *>(rec + R::QG + ((i * NCB + w) * 64 + l) * 16);
+        }
+    }
+    __device__ __forceinline__ void part3(Frags<K> &f, int w, int l) const {
+        using R = Rec<K>;
+        constexpr int NCB = K / 32;
+        if (w < NCB) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    f.kgt[tt][ks] = *reinterpret_cast<const half8 *>(rec + R::KGT + (((2 * w + tt) * 2 + ks) * 64 + l) * 16);
+        }
+        f.p[0] = *reinterpret_cast<const half8 *>(rec + R::PM + (tri(w, 0) * 64 + l) * 16);
+        if (w >= 2) f.p[1] = *reinterpret_cast<const half8 *>(rec + R::PM + (tri(w, 1) * 64 + l) * 16);
+    }
+};
 
 template <int K, int V, typename TOut>
 struct ScanSmem {
@@ -463,10 +486,11 @@ struct ScanSmem {
     float sig[2][NCB][64];    // sig_w of the lane's column
     float vT[2][16][kC + 4];
     float bet[2][kC];
-    half8 t[2][6][64];  // T fragments of the current / next chunk
+    float gam[2][K];
+    half8 t[2][6][64];        // T fragments of the current / next chunk
 };
 
-// Stage chunk data that every wave needs (V transposed, beta) into LDS buffer b.
+// Stage the chunk data that every wave needs (V transposed, beta, e^{G_n}, T) into LDS buffer b.
 template <int K, int V, typename TOut>
 __device__ __forceinline__ void stage(ScanSmem<K, V, TOut> &sm, int b, const Frags<K> &f, int tid) {
     const int stok = tid >> 2, sc4 = (tid & 3) * 4;
@@ -474,21 +498,27 @@ __device__ __forceinline__ void stage(ScanSmem<K, V, TOut> &sm, int b, const Fra
     sm.vT[b][sc4 + 1][stok] = f.v.y;
     sm.vT[b][sc4 + 2][stok] = f.v.z;
     sm.vT[b][sc4 + 3][stok] = f.v.w;
-    if (tid < kC) sm.bet[b][tid] = f.bet;
+    if (tid < 64) sm.bet[b][tid] = f.aux;
+    else if (tid < 64 + K) sm.gam[b][tid - 64] = f.aux;
     const int w = tid >> 6, l = tid & 63;
     sm.t[b][w][l] = f.t[0];
     if (w < 2) sm.t[b][w + 4][l] = f.t[1];
 }
 
-// One chunk of the state pass; `f` holds chunk c's operands, V/beta already
-// staged in LDS buffer `buf`. Ends by staging `fn` (chunk c + 1) into buf ^ 1.
+#define KDA_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// One chunk of the state pass. `f` holds chunk c's operands (V, beta, e^{G_n}
+// and T already staged in LDS buffer `buf`); the loads of the next chunk into
+// `fn` are issued in parts between the phases. Returns the output rows
+// 16w + 4g + e of column j0 + r in `out`.
 template <int K, int V, typename TOut>
-__device__ __forceinline__ void scan_chunk(ScanSmem<K, V, TOut> &sm, const Frags<K> &f, const Frags<K> &fn,
-                                           f4 (&S)[2], int buf, bool more, int t0, int nt, int H, int h,
-                                           int j0, TOut *og, float scale, int tid, int w, int l, int r,
-                                           int g) {
+__device__ __forceinline__ void scan_chunk(ScanSmem<K, V, TOut> &sm, const Frags<K> &f, Frags<K> &fn,
+                                           const FragLoader<K, V> &ld, f4 (&S)[2], int buf, float scale,
+                                           int tid, int w, int l, int r, int g, f4 &out) {
     constexpr int NCB = K / 32;
     const bool hasS = w < NCB;
+    ld.part0(fn, tid, w, l);
+    KDA_SCHED_FENCE();
     // (a) partial products with this wave's channel block of the state
     if (hasS) {
         float m = 0.f;
@@ -509,6 +539,9 @@ __device__ __forceinline__ void scan_chunk(ScanSmem<K, V, TOut> &sm, const Frags
         }
         sm.sig[buf][w][l] = sig;
     }
+    KDA_SCHED_FENCE();
+    ld.part1(fn, w, l);
+    KDA_SCHED_FENCE();
     __syncthreads();
 
     // (b) X = Diag(beta)(V - (K.e^G) S) for all 64 tokens, column j0 + r
@@ -539,6 +572,9 @@ __device__ __forceinline__ void scan_chunk(ScanSmem<K, V, TOut> &sm, const Frags
             xf[ks][4 + e] = static_cast<_Float16>(X[2 * ks + 1][e] * invx);
         }
 
+    KDA_SCHED_FENCE();
+    ld.part2(fn, w, l);
+    KDA_SCHED_FENCE();
     // (c) U' = T X
     f4 U[4];
     U[0] = mfma(sm.t[buf][0][l], xf[0], zero4());
@@ -563,11 +599,15 @@ __device__ __forceinline__ void scan_chunk(ScanSmem<K, V, TOut> &sm, const Frags
             uf[ks][4 + e] = static_cast<_Float16>(U[2 * ks + 1][e] * ru);
         }
 
+    KDA_SCHED_FENCE();
+    ld.part3(fn, w, l);
+    KDA_SCHED_FENCE();
     // (d) S <- Diag(e^{G_n}) S + (K.e^{G_n-G})^T U'
     if (hasS) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            f4 acc = S[tt] * f.gam[tt] * invu;
+            const f4 gm = *reinterpret_cast<const f4 *>(&sm.gam[buf][16 * (2 * w + tt) + 4 * g]);
+            f4 acc = S[tt] * gm * invu;
             acc = mfma(f.kgt[tt][0], uf[0], acc);
             acc = mfma(f.kgt[tt][1], uf[1], acc);
             S[tt] = acc * sigu;
@@ -581,15 +621,8 @@ __device__ __forceinline__ void scan_chunk(ScanSmem<K, V, TOut> &sm, const Frags
         for (int ww = 1; ww < NCB; ++ww) ov += sm.partO[buf][ww][w][l] * sw[ww];
         f4 pu = mfma(f.p[0], uf[0], zero4());
         if (w >= 2) pu = mfma(f.p[1], uf[1], pu);
-        ov = (ov + pu * sigu) * scale;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int tok = 16 * w + 4 * g + e;
-            if (tok < nt) io<TOut>::store(og + (static_cast<size_t>(t0 + tok) * H + h) * V + j0 + r, ov[e]);
-        }
+        out = (ov + pu * sigu) * scale;
     }
-    // the buffer of the next chunk was last read before this chunk's barrier
-    if (more) stage<K, V, TOut>(sm, buf ^ 1, fn, tid);
 }
 
 template <int K, int V, typename TOut>
@@ -623,22 +656,43 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillArgs a, const int32_t 
     TOut *og = static_cast<TOut *>(a.o);
 
     if (cbeg < cend) {
-        // operands of the next chunk are loaded while the current one is processed;
-        // the copy at the top of the loop waits for loads issued one chunk earlier
+        // operands of chunk c + 1 load while chunk c is processed; the copy at the
+        // top of the loop waits for loads issued one chunk earlier
         Frags<K> nx;
         const int clast = cend - 1;
-        load_frags<K, V>(nx, recs, nc, cbeg, clast, H, h, vg, tbeg, tend, cbeg, j0, tid, w, l, g);
-        stage<K, V, TOut>(sm, 0, nx, tid);
-        __syncthreads();
+        {
+            const FragLoader<K, V> ld(recs, nc, cbeg, clast, H, h, vg, tbeg, tend, cbeg, j0, tid);
+            ld.part0(nx, tid, w, l);
+            ld.part1(nx, w, l);
+            ld.part2(nx, w, l);
+            ld.part3(nx, w, l);
+        }
+
+        // The output of chunk c is stored at the start of iteration c + 1, after the
+        // wait for the prefetched operands: stores and loads share one completion
+        // counter, so a store issued just before that wait would stall it.
+        auto store_out = [&](int c, const f4 &ov) {
+            const int t0 = tbeg + (c - cbeg) * kC;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int tok = t0 + 16 * w + 4 * g + e;
+                if (tok < tend) io<TOut>::store(og + (static_cast<size_t>(tok) * H + h) * V + j0 + r, ov[e]);
+            }
+        };
+        f4 out = zero4();
         int buf = 0;
         for (int c = cbeg; c < cend; ++c, buf ^= 1) {
             const Frags<K> cu = nx;
-            load_frags<K, V>(nx, recs, nc, c + 1, clast, H, h, vg, tbeg, tend, cbeg, j0, tid, w, l, g);
-            __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the chunk's work
-            const int t0 = tbeg + (c - cbeg) * kC;
-            scan_chunk<K, V, TOut>(sm, cu, nx, S, buf, c + 1 < cend, t0, min(kC, tend - t0), H, h, j0, og,
-                                   a.scale, tid, w, l, r, g);
+            // Chunk c's shared data goes to LDS buffer c & 1 before chunk c's barrier.
+            // That buffer was last read by chunk c - 2; a wave that reaches this point
+            // has passed chunk c - 1's barrier, which no wave reaches before it has
+            // finished chunk c - 2, so the writes cannot overtake those reads.
+            stage<K, V, TOut>(sm, buf, cu, tid);
+            if (c > cbeg) store_out(c - 1, out);
+            const FragLoader<K, V> ld(recs, nc, c + 1, clast, H, h, vg, tbeg, tend, cbeg, j0, tid);
+            scan_chunk<K, V, TOut>(sm, cu, nx, ld, S, buf, a.scale, tid, w, l, r, g, out);
         }
+        store_out(cend - 1, out);
     }
     if (hasS && a.sT) {
 #pragma unroll
