@@ -39,6 +39,9 @@
 // uses k(g, e) = 4g + e for e < 4 and 16 + 4g + (e - 4) for e >= 4, which is
 // exactly the set of rows a lane holds of two stacked 16x16 results, so a
 // product's result feeds the next product's B operand from registers.
+#include <algorithm>
+#include <cstdlib>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -47,6 +50,7 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 constexpr int kC = 64;
 constexpr float kFastRange = 10.f;  // max decay exponent of one sub-chunk on the fp16 path
@@ -110,32 +114,47 @@ __host__ __device__ __forceinline__ size_t a_nc(const PrefillArgs &a) {
 }
 
 // ---------------------------------------------------------------------------
-// chunk offsets: off[n] = sum_{m<n} ceil(len_m / 64), off[N] = total chunks
-__global__ __launch_bounds__(256) void chunk_offsets_kernel(const int32_t *cu, int32_t N,
-                                                             int32_t *off) {
-    __shared__ int32_t buf[256];
-    __shared__ int32_t carry;
+// chunk and segment offsets: off[n] = sum_{m<n} ceil(len_m / 64), off[N] = total
+// chunks; soff[n] = sum_{m<n} G_m with G_m = max(1, ceil(chunks_m / L)) segments
+__global__ __launch_bounds__(256) void chunk_offsets_kernel(const int32_t *cu, int32_t N, int32_t L,
+                                                             int32_t *off, int32_t *soff) {
+    __shared__ int32_t buf[2][256];
+    __shared__ int32_t carry[2];
     const int t = threadIdx.x;
-    if (t == 0) carry = 0;
+    if (t < 2) carry[t] = 0;
     __syncthreads();
     for (int base = 0; base < N; base += 256) {
         const int n = base + t;
-        int nc = 0;
-        if (n < N) nc = (max(cu[n + 1] - cu[n], 0) + kC - 1) / kC;
-        buf[t] = nc;
+        int nc = 0, ns = 0;
+        if (n < N) {
+            nc = (max(cu[n + 1] - cu[n], 0) + kC - 1) / kC;
+            ns = max(1, (nc + L - 1) / L);
+        }
+        buf[0][t] = nc;
+        buf[1][t] = ns;
         __syncthreads();
-        for (int s = 1; s < 256; s <<= 1) {
-            const int x = t >= s ? buf[t - s] : 0;
+        for (int d = 1; d < 256; d <<= 1) {
+            const int x0 = t >= d ? buf[0][t - d] : 0, x1 = t >= d ? buf[1][t - d] : 0;
             __syncthreads();
-            buf[t] += x;
+            buf[0][t] += x0;
+            buf[1][t] += x1;
             __syncthreads();
         }
-        if (n < N) off[n] = carry + buf[t] - nc;
+        if (n < N) {
+            off[n] = carry[0] + buf[0][t] - nc;
+            soff[n] = carry[1] + buf[1][t] - ns;
+        }
         __syncthreads();
-        if (t == 255) carry += buf[255];
+        if (t == 255) {
+            carry[0] += buf[0][255];
+            carry[1] += buf[1][255];
+        }
         __syncthreads();
     }
-    if (t == 0) off[N] = carry;
+    if (t == 0) {
+        off[N] = carry[0];
+        soff[N] = carry[1];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -408,332 +427,564 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a, const int32_t 
 }
 
 // ---------------------------------------------------------------------------
-// scan: sequential pass over the chunks of one (sequence, head, 16 value columns)
-template <int K>
-struct Frags {
-    float4 v;              // this thread's 4 columns of one token of V        (staged to LDS)
-    float aux;             // beta (threads 0..63) or e^{G_n} (threads 64..191) (staged to LDS)
-    half8 t[2];            // T fragments w and w + 4 (w + 4 exists for w < 2)  (staged to LDS)
-    half8 kexp[4], qg[4];  // this wave's channel block, all four token row blocks
-    half8 kgt[2][2];       // this wave's two channel tiles x two token steps
-    half8 p[2];            // this wave's output row block
+// State passes. The chunks of a sequence are cut into segments of L consecutive
+// chunks. Every chunk maps its incoming state affinely,
+//   S <- (Diag(e^{G_n}) - (K.e^{G_n-G})^T T Diag(beta) (K.e^G)) S + (K.e^{G_n-G})^T T Diag(beta) V,
+// so a segment does too: S_out = M S_in + N, with M (d_k x d_k) the segment run
+// from the identity with V = 0 and N (d_k x d_v) the segment run from zero.
+//  * seg_kernel, every segment but the last of each sequence, in parallel:
+//    segment 0 runs from the initial state (its end state enters segment 1), a
+//    middle segment runs once for M and once for N (two workgroups);
+//  * prefix_kernel: S_in(g + 1) = M_g S_in(g) + N_g along the middle segments;
+//  * out_kernel, every segment in parallel from its incoming state, with outputs;
+//    the last segment of a sequence writes the final state.
+// A workgroup is four waves over all columns of one (segment, head) state (or of
+// M or N); each wave holds 16 NB columns x d_k rows in MFMA accumulators. A
+// chunk's record is copied global -> LDS once per workgroup with direct-to-LDS
+// loads, one chunk ahead, into a two-buffer ring, so that no record is streamed
+// by more than one compute unit at a time.
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kPad = 32;  // bytes after every 1 KB LDS copy of V or O rows: 4-row groups hit distinct banks
+
+// 64 x V bf16 tile (V, or the output) in LDS: copies of 1 KB (1024 / 2V token rows) + padding
+template <int V>
+struct VTile {
+    static constexpr int RPI = 1024 / (2 * V);
+    static constexpr int NI = kC / RPI;
+    static constexpr int BYTES = NI * (1024 + kPad);
+    __device__ __forceinline__ static int off(int t, int col) {
+        return (t / RPI) * (1024 + kPad) + (t % RPI) * (2 * V) + 2 * col;
+    }
 };
 
-// Operand loads of chunk c (clamped to the last chunk, so they are unconditional),
-// in four parts that the chunk loop spreads over the previous chunk's work: one
-// burst of all of them saturates the CU's vector memory pipeline.
 template <int K, int V>
-struct FragLoader {
-    const char *rec;
-    const bf16_t *vrow;
-    bool vok;
-
-    __device__ __forceinline__ FragLoader(const char *recs, size_t nc, int c, int clast, int H, int h,
-                                          const bf16_t *vg, int tbeg, int tend, int cbeg, int j0, int tid) {
-        c = min(c, clast);
-        rec = recs + (static_cast<size_t>(h) * nc + c) * Rec<K>::BYTES;
-        const int tok = tbeg + (c - cbeg) * kC + (tid >> 2);
-        vok = tok < tend;
-        vrow = vg + (static_cast<size_t>(min(tok, tend - 1)) * H + h) * V + j0 + (tid & 3) * 4;
-    }
-    __device__ __forceinline__ void part0(Frags<K> &f, int tid, int w, int l) const {
-        using R = Rec<K>;
-        const float4 vv = io<bf16_t>::load4(vrow);
-        f.v = vok ? vv : make_float4(0.f, 0.f, 0.f, 0.f);
-        if (tid < 64) f.aux = reinterpret_cast<const float *>(rec + R::BET)[tid];
-        else if (tid < 64 + K) f.aux = reinterpret_cast<const float *>(rec + R::GAM)[tid - 64];
-        f.t[0] = *reinterpret_cast<const half8 *>(rec + R::TM + (w * 64 + l) * 16);
-        if (w < 2) f.t[1] = *reinterpret_cast<const half8 *>(rec + R::TM + ((w + 4) * 64 + l) * 16);
-    }
-    __device__ __forceinline__ void part1(Frags<K> &f, int w, int l) const {
-        using R = Rec<K>;
-        constexpr int NCB = K / 32;
-        if (w < NCB) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                f.kexp[i] = *reinterpret_cast<const half8 *>(rec + R::KEXP + ((i * NCB + w) * 64 + l) * 16);
-        }
-    }
-    __device__ __forceinline__ void part2(Frags<K> &f, int w, int l) const {
-        using R = Rec<K>;
-        constexpr int NCB = K / 32;
-        if (w < NCB) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                f.qg[i] = *reinterpret_cast<const half8 *>(rec + R::QG + ((i * NCB + w) * 64 + l) * 16);
-        }
-    }
-    __device__ __forceinline__ void part3(Frags<K> &f, int w, int l) const {
-        using R = Rec<K>;
-        constexpr int NCB = K / 32;
-        if (w < NCB) {
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    f.kgt[tt][ks] = *reinterpret_cast<const half8 *>(rec + R::KGT + (((2 * w + tt) * 2 + ks) * 64 + l) * 16);
-        }
-        f.p[0] = *reinterpret_cast<const half8 *>(rec + R::PM + (tri(w, 0) * 64 + l) * 16);
-        if (w >= 2) f.p[1] = *reinterpret_cast<const half8 *>(rec + R::PM + (tri(w, 1) * 64 + l) * 16);
-    }
+struct ScanBuf {
+    static constexpr int VT = static_cast<int>(Rec<K>::BYTES);
+    static constexpr int BYTES = VT + VTile<V>::BYTES;
 };
 
-template <int K, int V, typename TOut>
-struct ScanSmem {
-    static constexpr int NCB = K / 32;
-    f4 partX[2][NCB][4][64];  // (K.e^G) S_w / sig_w per wave w (channel block)
-    f4 partO[2][NCB][4][64];  // (Q.e^G) S_w / sig_w
-    float sig[2][NCB][64];    // sig_w of the lane's column
-    float vT[2][16][kC + 4];
-    float bet[2][kC];
-    float gam[2][K];
-    half8 t[2][6][64];        // T fragments of the current / next chunk
-};
-
-// Stage the chunk data that every wave needs (V transposed, beta, e^{G_n}, T) into LDS buffer b.
-template <int K, int V, typename TOut>
-__device__ __forceinline__ void stage(ScanSmem<K, V, TOut> &sm, int b, const Frags<K> &f, int tid) {
-    const int stok = tid >> 2, sc4 = (tid & 3) * 4;
-    sm.vT[b][sc4 + 0][stok] = f.v.x;
-    sm.vT[b][sc4 + 1][stok] = f.v.y;
-    sm.vT[b][sc4 + 2][stok] = f.v.z;
-    sm.vT[b][sc4 + 3][stok] = f.v.w;
-    if (tid < 64) sm.bet[b][tid] = f.aux;
-    else if (tid < 64 + K) sm.gam[b][tid - 64] = f.aux;
-    const int w = tid >> 6, l = tid & 63;
-    sm.t[b][w][l] = f.t[0];
-    if (w < 2) sm.t[b][w + 4][l] = f.t[1];
-}
-
-#define KDA_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
-
-// One chunk of the state pass. `f` holds chunk c's operands (V, beta, e^{G_n}
-// and T already staged in LDS buffer `buf`); the loads of the next chunk into
-// `fn` are issued in parts between the phases. Returns the output rows
-// 16w + 4g + e of column j0 + r in `out`.
-template <int K, int V, typename TOut>
-__device__ __forceinline__ void scan_chunk(ScanSmem<K, V, TOut> &sm, const Frags<K> &f, Frags<K> &fn,
-                                           const FragLoader<K, V> &ld, f4 (&S)[2], int buf, float scale,
-                                           int tid, int w, int l, int r, int g, f4 &out) {
-    constexpr int NCB = K / 32;
-    const bool hasS = w < NCB;
-    ld.part0(fn, tid, w, l);
-    KDA_SCHED_FENCE();
-    // (a) partial products with this wave's channel block of the state
-    if (hasS) {
-        float m = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(fabsf(S[0][e]), fabsf(S[1][e])));
-        float inv;
-        const float sig = col_scale(col_max(m), inv);
-        half8 sf;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            sf[e] = static_cast<_Float16>(S[0][e] * inv);
-            sf[4 + e] = static_cast<_Float16>(S[1][e] * inv);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sm.partX[buf][w][i][l] = mfma(f.kexp[i], sf, zero4());
-            sm.partO[buf][w][i][l] = mfma(f.qg[i], sf, zero4());
-        }
-        sm.sig[buf][w][l] = sig;
+// Copy chunk data into LDS buffer `dst`, spread over the four waves: the record
+// fragments the pass reads (all of them with outputs, else K.e^G, its transpose
+// with e^{G_n-G}, and T), e^{G_n} and beta, and (HASV) the 64 x V tile of V.
+// Tokens past the sequence end read the last token (finite; beta is 0 there).
+template <int K, int V, bool FULL, bool HASV>
+__device__ __forceinline__ void copy_chunk(char *dst, const char *rec, const bf16_t *vg, int t0, int tend,
+                                           int H, int h, int w, int l) {
+    using R = Rec<K>;
+    constexpr int NKX = 4 * (K / 32);
+    constexpr int KG0 = static_cast<int>(R::KGT / 1024);
+    constexpr int NF = FULL ? static_cast<int>(R::GAM / 1024) : NKX + 2 * (K / 16) + 6;
+    for (int f = w; f < NF; f += 4) {
+        const int fi = (FULL || f < NKX) ? f : f - NKX + KG0;
+        __builtin_amdgcn_global_load_lds(rec + fi * 1024 + l * 16, (lds_void *)(dst + fi * 1024), 16, 0, 0);
     }
-    KDA_SCHED_FENCE();
-    ld.part1(fn, w, l);
-    KDA_SCHED_FENCE();
-    __syncthreads();
-
-    // (b) X = Diag(beta)(V - (K.e^G) S) for all 64 tokens, column j0 + r
-    f4 X[4];
-    float mx = 0.f;
-    float sw[NCB];
-#pragma unroll
-    for (int ww = 0; ww < NCB; ++ww) sw[ww] = sm.sig[buf][ww][l];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f4 ks = sm.partX[buf][0][i][l] * sw[0];
-#pragma unroll
-        for (int ww = 1; ww < NCB; ++ww) ks += sm.partX[buf][ww][i][l] * sw[ww];
-        const f4 vv = *reinterpret_cast<const f4 *>(&sm.vT[buf][r][16 * i + 4 * g]);
-        const f4 bb = *reinterpret_cast<const f4 *>(&sm.bet[buf][16 * i + 4 * g]);
-        X[i] = bb * (vv - ks);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(X[i][e]));
+    // e^{G_n} [K] and beta [64], fp32: K + 64 words, 4 bytes per lane; the instruction
+    // offset applies to both the global and the LDS address
+    static_assert(R::BET + 4 * kC == R::GAM + 256 * ((K + kC) / 64), "gamma + beta span");
+    if (w == 0) {
+        const char *src = rec + R::GAM + l * 4;
+        __builtin_amdgcn_global_load_lds(src, (lds_void *)(dst + R::GAM), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(src, (lds_void *)(dst + R::GAM), 4, 256, 0);
+        if (K == 128) __builtin_amdgcn_global_load_lds(src, (lds_void *)(dst + R::GAM), 4, 512, 0);
     }
-    float invx;
-    const float sigx = col_scale(col_max(mx), invx);
-    half8 xf[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            xf[ks][e] = static_cast<_Float16>(X[2 * ks][e] * invx);
-            xf[ks][4 + e] = static_cast<_Float16>(X[2 * ks + 1][e] * invx);
+    if (HASV) {
+        using VT = VTile<V>;
+        constexpr int LPR = 2 * V / 16;  // lanes per token row
+        for (int q = w; q < VT::NI; q += 4) {
+            const int tok = min(t0 + q * VT::RPI + l / LPR, tend - 1);
+            __builtin_amdgcn_global_load_lds(vg + (static_cast<size_t>(tok) * H + h) * V + (l % LPR) * 8,
+                                             (lds_void *)(dst + ScanBuf<K, V>::VT + q * (1024 + kPad)), 16, 0, 0);
         }
-
-    KDA_SCHED_FENCE();
-    ld.part2(fn, w, l);
-    KDA_SCHED_FENCE();
-    // (c) U' = T X
-    f4 U[4];
-    U[0] = mfma(sm.t[buf][0][l], xf[0], zero4());
-    U[1] = mfma(sm.t[buf][1][l], xf[0], zero4());
-    U[2] = mfma(sm.t[buf][3][l], xf[1], mfma(sm.t[buf][2][l], xf[0], zero4()));
-    U[3] = mfma(sm.t[buf][5][l], xf[1], mfma(sm.t[buf][4][l], xf[0], zero4()));
-    // U holds U' / sigx; pick U' / sigu with the column maximum of U' in [2^14, 2^15)
-    float mu = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mu = fmaxf(mu, fabsf(U[i][e]));
-    float invu;
-    const float sigu = col_scale(col_max(mu) * sigx, invu);
-    const float ru = sigx * invu;
-    half8 uf[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            uf[ks][e] = static_cast<_Float16>(U[2 * ks][e] * ru);
-            uf[ks][4 + e] = static_cast<_Float16>(U[2 * ks + 1][e] * ru);
-        }
-
-    KDA_SCHED_FENCE();
-    ld.part3(fn, w, l);
-    KDA_SCHED_FENCE();
-    // (d) S <- Diag(e^{G_n}) S + (K.e^{G_n-G})^T U'
-    if (hasS) {
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const f4 gm = *reinterpret_cast<const f4 *>(&sm.gam[buf][16 * (2 * w + tt) + 4 * g]);
-            f4 acc = S[tt] * gm * invu;
-            acc = mfma(f.kgt[tt][0], uf[0], acc);
-            acc = mfma(f.kgt[tt][1], uf[1], acc);
-            S[tt] = acc * sigu;
-        }
-    }
-
-    // (e) O rows of token block w = (Q.e^G) S + P U'
-    {
-        f4 ov = sm.partO[buf][0][w][l] * sw[0];
-#pragma unroll
-        for (int ww = 1; ww < NCB; ++ww) ov += sm.partO[buf][ww][w][l] * sw[ww];
-        f4 pu = mfma(f.p[0], uf[0], zero4());
-        if (w >= 2) pu = mfma(f.p[1], uf[1], pu);
-        out = (ov + pu * sigu) * scale;
     }
 }
 
-template <int K, int V, typename TOut>
-__global__ __launch_bounds__(256) void scan_kernel(PrefillArgs a, const int32_t *off, const char *recs) {
-    constexpr int NCB = K / 32, NV = V / 16;
-    __shared__ ScanSmem<K, V, TOut> sm;
+__device__ __forceinline__ half8 lds_frag(const char *buf, size_t off, int l) {
+    return *reinterpret_cast<const half8 *>(buf + off + l * 16);
+}
 
-    // blockIdx -> (unit, value tile) with the NV tiles of a unit on one XCD
-    const int bid = blockIdx.x, xcd = bid & 7, q8 = bid >> 3;
-    const int vt = q8 % NV, unit = (q8 / NV) * 8 + xcd;
-    if (unit >= a.N * a.H) return;
-    const int n = unit / a.H, h = unit - (unit / a.H) * a.H, j0 = vt * 16;
+// Workgroup barrier without a memory fence: callers wait for the counters they
+// need first (a fence would also wait for the copies in flight into the other buffer).
+__device__ __forceinline__ void wg_barrier() {
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }         // vm, exp, lgkm = 0
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }    // lgkmcnt(0)
+
+// One chunk for one wave holding NB 16-column blocks of the state, S[j][ct] =
+// rows 16 ct + 4g + e of column col0 + 16 j + r. part_a: column scales of the
+// state, (K.e^G) S and (OUT) (Q.e^G) S, and X = Diag(beta)(V - (K.e^G) S) as
+// scaled fp16 operands (V = 0 without HASV). part_b: U' = T X, the state update
+// and (OUT) the outputs O = (Q.e^G) S + P U' of tokens 16i + 4g + e in out[j][i].
+template <int K, int V, int NB, bool OUT, bool HASV>
+struct ChunkStep {
+    static constexpr int NCB = K / 32, NCT = K / 16;
+    using R = Rec<K>;
+    float sigs[NB], sigx[NB];
+    half8 xf[NB][2];
+    f4 oa[NB][4];
+
+    __device__ __forceinline__ void part_a(const char *buf, const f4 (&S)[NB][NCT], int col0, int l, int r, int g) {
+        half8 sf[NB][NCB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            float m = 0.f;
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(S[j][ct][e]));
+            float inv;
+            sigs[j] = col_scale(col_max(m), inv);
+#pragma unroll
+            for (int kb = 0; kb < NCB; ++kb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sf[j][kb][e] = static_cast<_Float16>(S[j][2 * kb][e] * inv);
+                    sf[j][kb][4 + e] = static_cast<_Float16>(S[j][2 * kb + 1][e] * inv);
+                }
+        }
+        f4 xa[NB][4];
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                xa[j][i] = zero4();
+                if (OUT) oa[j][i] = zero4();
+            }
+#pragma unroll
+        for (int kb = 0; kb < NCB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const half8 kx = lds_frag(buf, R::KEXP + (i * NCB + kb) * 1024, l);
+#pragma unroll
+                for (int j = 0; j < NB; ++j) xa[j][i] = mfma(kx, sf[j][kb], xa[j][i]);
+                if (OUT) {
+                    const half8 qx = lds_frag(buf, R::QG + (i * NCB + kb) * 1024, l);
+#pragma unroll
+                    for (int j = 0; j < NB; ++j) oa[j][i] = mfma(qx, sf[j][kb], oa[j][i]);
+                }
+            }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            f4 X[4];
+            float mx = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f4 bb = *reinterpret_cast<const f4 *>(buf + R::BET + (16 * i + 4 * g) * 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float vv = 0.f;
+                    if (HASV)
+                        vv = bf16_to_f32(*reinterpret_cast<const bf16_t *>(
+                            buf + ScanBuf<K, V>::VT + VTile<V>::off(16 * i + 4 * g + e, col0 + 16 * j + r)));
+                    X[i][e] = bb[e] * fmaf(-sigs[j], xa[j][i][e], vv);
+                    mx = fmaxf(mx, fabsf(X[i][e]));
+                }
+            }
+            float invx;
+            sigx[j] = col_scale(col_max(mx), invx);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    xf[j][ks][e] = static_cast<_Float16>(X[2 * ks][e] * invx);
+                    xf[j][ks][4 + e] = static_cast<_Float16>(X[2 * ks + 1][e] * invx);
+                }
+        }
+    }
+
+    __device__ __forceinline__ void part_b(const char *buf, f4 (&S)[NB][NCT], f4 (&out)[NB][4], float scale, int l,
+                                           int g) {
+        half8 tm[6];
+#pragma unroll
+        for (int f = 0; f < 6; ++f) tm[f] = lds_frag(buf, R::TM + f * 1024, l);
+        half8 uf[NB][2];
+        float sigu[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            // U' = T X, held as U' / sigx
+            f4 U[4];
+            U[0] = mfma(tm[0], xf[j][0], zero4());
+            U[1] = mfma(tm[1], xf[j][0], zero4());
+            U[2] = mfma(tm[3], xf[j][1], mfma(tm[2], xf[j][0], zero4()));
+            U[3] = mfma(tm[5], xf[j][1], mfma(tm[4], xf[j][0], zero4()));
+            float mu = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mu = fmaxf(mu, fabsf(U[i][e]));
+            float invu;
+            sigu[j] = col_scale(col_max(mu) * sigx[j], invu);
+            const float ru = sigx[j] * invu;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    uf[j][ks][e] = static_cast<_Float16>(U[2 * ks][e] * ru);
+                    uf[j][ks][4 + e] = static_cast<_Float16>(U[2 * ks + 1][e] * ru);
+                }
+        }
+        // S <- Diag(e^{G_n}) S + (K.e^{G_n-G})^T U'
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const f4 gm = *reinterpret_cast<const f4 *>(buf + R::GAM + (16 * ct + 4 * g) * 4);
+            const half8 k0 = lds_frag(buf, R::KGT + (ct * 2 + 0) * 1024, l);
+            const half8 k1 = lds_frag(buf, R::KGT + (ct * 2 + 1) * 1024, l);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const f4 acc = mfma(k1, uf[j][1], mfma(k0, uf[j][0], zero4()));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) S[j][ct][e] = fmaf(sigu[j], acc[e], S[j][ct][e] * gm[e]);
+            }
+        }
+        if (OUT) {
+            // O = (Q.e^G) S + P U'
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const half8 p0 = lds_frag(buf, R::PM + tri(i, 0) * 1024, l);
+                half8 p1 = p0;
+                if (i >= 2) p1 = lds_frag(buf, R::PM + tri(i, 1) * 1024, l);
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    f4 pu = mfma(p0, uf[j][0], zero4());
+                    if (i >= 2) pu = mfma(p1, uf[j][1], pu);
+                    const float os = sigs[j] * scale, ou = sigu[j] * scale;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) out[j][i][e] = fmaf(oa[j][i][e], os, pu[e] * ou);
+                }
+            }
+        }
+    }
+};
+
+// The chunks [cb, ce) of one segment (tokens from tbeg; the sequence ends at tend)
+// for the wave's state columns col0 .. col0 + 16 NB - 1. With OUT, the outputs of
+// every chunk go to `og`: bf16 through an LDS tile in the V region of the chunk's
+// buffer (written once all waves have read V, stored by whole rows at the next
+// chunk), fp32 directly from the registers.
+template <int K, int V, int NB, bool OUT, bool HASV, typename TOut>
+__device__ __forceinline__ void run_segment(char *lb0, char *lb1, f4 (&S)[NB][K / 16], const char *hrec, int cb,
+                                            int ce, int tbeg, int tend, const bf16_t *vg, TOut *og, int H, int h,
+                                            float scale, int tid, int w, int l, int r, int g, int col0) {
+    constexpr size_t RB = Rec<K>::BYTES;
+    constexpr bool TILE = OUT && sizeof(TOut) == 2;
+    constexpr int NP = kC * 2 * V / 16 / 256;  // 16-byte output pieces per thread
+    using VT = VTile<V>;
+    if (cb >= ce) return;
+    f4 out[NB][4];
+    copy_chunk<K, V, OUT, HASV>(lb0, hrec + static_cast<size_t>(cb) * RB, vg, tbeg, tend, H, h, w, l);
+
+    auto body = [&](char *cur, char *oth, int c) {
+        const int tc = tbeg + (c - cb) * kC;
+        wait_all();  // this wave's copies of chunk c, its stores and its LDS writes are done
+        wg_barrier();
+        u4 pc[NP];
+        if (TILE && c > cb) {
+#pragma unroll
+            for (int q = 0; q < NP; ++q) {
+                const int p = q * 256 + tid, row = p / (2 * V / 16), pi = p % (2 * V / 16);
+                pc[q] = *reinterpret_cast<const u4 *>(oth + ScanBuf<K, V>::VT + VT::off(row, pi * 8));
+            }
+            wait_lds();
+        }
+        if (TILE) wg_barrier();  // every wave has read the previous output tile out of `oth`
+        if (c + 1 < ce)
+            copy_chunk<K, V, OUT, HASV>(oth, hrec + static_cast<size_t>(c + 1) * RB, vg, tc + kC, tend, H, h, w, l);
+        if (TILE && c > cb) {
+#pragma unroll
+            for (int q = 0; q < NP; ++q) {
+                const int p = q * 256 + tid, row = p / (2 * V / 16), pi = p % (2 * V / 16);
+                const int tok = tc - kC + row;
+                if (tok < tend) *reinterpret_cast<u4 *>(og + (static_cast<size_t>(tok) * H + h) * V + pi * 8) = pc[q];
+            }
+        }
+        ChunkStep<K, V, NB, OUT, HASV> st;
+        st.part_a(cur, S, col0, l, r, g);
+        if (TILE) wg_barrier();  // every wave has read V of chunk c: its region takes the outputs
+        st.part_b(cur, S, out, scale, l, g);
+        if (OUT) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = 16 * i + 4 * g + e, col = col0 + 16 * j + r;
+                        if (TILE) {
+                            *reinterpret_cast<bf16_t *>(cur + ScanBuf<K, V>::VT + VT::off(t, col)) =
+                                f32_to_bf16(out[j][i][e]);
+                        } else if (tc + t < tend) {
+                            io<TOut>::store(og + (static_cast<size_t>(tc + t) * H + h) * V + col, out[j][i][e]);
+                        }
+                    }
+        }
+    };
+    // two chunks per iteration, so that each buffer is a distinct LDS object: copies
+    // into one never make reads of the other wait
+    for (int c = cb; c < ce; c += 2) {
+        body(lb0, lb1, c);
+        if (c + 1 >= ce) break;
+        body(lb1, lb0, c + 1);
+    }
+    if (TILE) {
+        wait_all();
+        wg_barrier();
+        const char *last = ((ce - 1 - cb) & 1) ? lb1 : lb0;
+        const int t0 = tbeg + (ce - 1 - cb) * kC;
+#pragma unroll
+        for (int q = 0; q < NP; ++q) {
+            const int p = q * 256 + tid, row = p / (2 * V / 16), pi = p % (2 * V / 16);
+            const int tok = t0 + row;
+            const u4 v = *reinterpret_cast<const u4 *>(last + ScanBuf<K, V>::VT + VT::off(row, pi * 8));
+            if (tok < tend) *reinterpret_cast<u4 *>(og + (static_cast<size_t>(tok) * H + h) * V + pi * 8) = v;
+        }
+    }
+}
+
+// state slice of a wave: S[j][ct][e] = X[16 ct + 4g + e][col0 + 16 j + r] of a row-major
+// d_k x ld matrix X (nullptr: zero)
+template <int K, int NB>
+__device__ __forceinline__ void load_state(f4 (&S)[NB][K / 16], const float *x, int ld, int col0, int r, int g) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int ct = 0; ct < K / 16; ++ct) S[j][ct] = zero4();
+    if (!x) return;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int ct = 0; ct < K / 16; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[j][ct][e] = x[static_cast<size_t>(16 * ct + 4 * g + e) * ld + col0 + 16 * j + r];
+}
+template <int K, int NB>
+__device__ __forceinline__ void store_state(const f4 (&S)[NB][K / 16], float *x, int ld, int col0, int r, int g) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int ct = 0; ct < K / 16; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[static_cast<size_t>(16 * ct + 4 * g + e) * ld + col0 + 16 * j + r] = S[j][ct][e];
+}
+
+// global segment s -> (sequence n, index gl inside it, segment count G of n)
+struct SegInfo {
+    int n, gl, G;
+};
+__device__ __forceinline__ SegInfo seg_of(const int32_t *soff, int N, int s) {
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (soff[mid] <= s) lo = mid; else hi = mid - 1;
+    }
+    return SegInfo{lo, s - soff[lo], soff[lo + 1] - soff[lo]};
+}
+
+struct SegBufs {
+    float *sin;   // [segments, H, d_k, d_v] incoming state of each segment
+    float *mapm;  // [segments, H, d_k, d_k] M of middle segments
+    float *mapn;  // [segments, H, d_k, d_v] N of middle segments
+};
+
+// blockIdx -> (segment s, head h, part): the two parts (M, N) of a middle segment
+// are 8 blocks apart, so they run on one XCD and share its L2 for the records
+template <int K, int V>
+__global__ __launch_bounds__(256) void seg_kernel(PrefillArgs a, const int32_t *off, const int32_t *soff, int L,
+                                                  const char *recs, SegBufs sb) {
+    __shared__ __attribute__((aligned(16))) char lb0[ScanBuf<K, V>::BYTES];
+    __shared__ __attribute__((aligned(16))) char lb1[ScanBuf<K, V>::BYTES];
+    const int bid = blockIdx.x, q8 = bid >> 3, part = q8 & 1, su = (q8 >> 1) * 8 + (bid & 7);
     const int H = a.H;
+    const int s = su / H, h = su - (su / H) * H;
+    if (s >= soff[a.N]) return;
+    const SegInfo si = seg_of(soff, a.N, s);
+    if (si.gl >= si.G - 1) return;    // the last segment has no successor
+    if (si.gl == 0 && part == 1) return;
     const int tid = threadIdx.x, l = tid & 63, r = l & 15, g = l >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool hasS = w < NCB;
-    const size_t sbase = (static_cast<size_t>(n) * H + h) * static_cast<size_t>(K) * V;
-
-    f4 S[2] = {zero4(), zero4()};  // S[16 (2w + tt) + 4g + e][j0 + r]
-    if (hasS && a.s0) {
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                S[tt][e] = a.s0[sbase + static_cast<size_t>(16 * (2 * w + tt) + 4 * g + e) * V + j0 + r];
-    }
-    const int cbeg = off[n], cend = off[n + 1];
-    const int tbeg = a.cu_seqlens[n], tend = a.cu_seqlens[n + 1];
-    const size_t nc = a_nc(a);
+    const int cb = off[si.n] + si.gl * L, ce = min(off[si.n + 1], cb + L);
+    const int tbeg = a.cu_seqlens[si.n] + si.gl * L * kC, tend = a.cu_seqlens[si.n + 1];
+    const char *hrec = recs + static_cast<size_t>(h) * a_nc(a) * Rec<K>::BYTES;
     const bf16_t *vg = static_cast<const bf16_t *>(a.v);
-    TOut *og = static_cast<TOut *>(a.o);
-
-    if (cbeg < cend) {
-        // operands of chunk c + 1 load while chunk c is processed; the copy at the
-        // top of the loop waits for loads issued one chunk earlier
-        Frags<K> nx;
-        const int clast = cend - 1;
-        {
-            const FragLoader<K, V> ld(recs, nc, cbeg, clast, H, h, vg, tbeg, tend, cbeg, j0, tid);
-            ld.part0(nx, tid, w, l);
-            ld.part1(nx, w, l);
-            ld.part2(nx, w, l);
-            ld.part3(nx, w, l);
-        }
-
-        // The output of chunk c is stored at the start of iteration c + 1, after the
-        // wait for the prefetched operands: stores and loads share one completion
-        // counter, so a store issued just before that wait would stall it.
-        auto store_out = [&](int c, const f4 &ov) {
-            const int t0 = tbeg + (c - cbeg) * kC;
+    const size_t skv = (static_cast<size_t>(s) * H + h) * K * V;
+    if (si.gl > 0 && part == 0) {
+        constexpr int NB = K / 64;
+        const int col0 = 16 * NB * w;
+        f4 S[NB][K / 16];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int tok = t0 + 16 * w + 4 * g + e;
-                if (tok < tend) io<TOut>::store(og + (static_cast<size_t>(tok) * H + h) * V + j0 + r, ov[e]);
-            }
-        };
-        f4 out = zero4();
-        int buf = 0;
-        for (int c = cbeg; c < cend; ++c, buf ^= 1) {
-            const Frags<K> cu = nx;
-            // Chunk c's shared data goes to LDS buffer c & 1 before chunk c's barrier.
-            // That buffer was last read by chunk c - 2; a wave that reaches this point
-            // has passed chunk c - 1's barrier, which no wave reaches before it has
-            // finished chunk c - 2, so the writes cannot overtake those reads.
-            stage<K, V, TOut>(sm, buf, cu, tid);
-            if (c > cbeg) store_out(c - 1, out);
-            const FragLoader<K, V> ld(recs, nc, c + 1, clast, H, h, vg, tbeg, tend, cbeg, j0, tid);
-            scan_chunk<K, V, TOut>(sm, cu, nx, ld, S, buf, a.scale, tid, w, l, r, g, out);
-        }
-        store_out(cend - 1, out);
-    }
-    if (hasS && a.sT) {
+        for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+            for (int ct = 0; ct < K / 16; ++ct)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                a.sT[sbase + static_cast<size_t>(16 * (2 * w + tt) + 4 * g + e) * V + j0 + r] = S[tt][e];
+                for (int e = 0; e < 4; ++e) S[j][ct][e] = (16 * ct + 4 * g + e == col0 + 16 * j + r) ? 1.f : 0.f;
+        run_segment<K, V, NB, false, false, float>(lb0, lb1, S, hrec, cb, ce, tbeg, tend, vg, nullptr, H, h, 1.f,
+                                                   tid, w, l, r, g, col0);
+        store_state<K, NB>(S, sb.mapm + (static_cast<size_t>(s) * H + h) * K * K, K, col0, r, g);
+    } else {
+        constexpr int NB = V / 64;
+        const int col0 = 16 * NB * w;
+        f4 S[NB][K / 16];
+        const float *init = nullptr;
+        if (si.gl == 0 && a.s0) init = a.s0 + (static_cast<size_t>(si.n) * H + h) * K * V;
+        load_state<K, NB>(S, init, V, col0, r, g);
+        // segment 0: a copy of the initial state for the output pass (final_state may alias it)
+        if (si.gl == 0) store_state<K, NB>(S, sb.sin + skv, V, col0, r, g);
+        run_segment<K, V, NB, false, true, float>(lb0, lb1, S, hrec, cb, ce, tbeg, tend, vg, nullptr, H, h, 1.f,
+                                                  tid, w, l, r, g, col0);
+        store_state<K, NB>(S, si.gl == 0 ? sb.sin + skv + static_cast<size_t>(H) * K * V : sb.mapn + skv, V, col0, r,
+                           g);
     }
 }
+
+// S_in(g + 1) = M_g S_in(g) + N_g for the middle segments g of one (sequence, head),
+// 16 state columns per workgroup, fp32
+template <int K, int V>
+__global__ __launch_bounds__(256) void prefix_kernel(const int32_t *soff, int N, int H, SegBufs sb) {
+    __shared__ float m[K][K + 4];
+    __shared__ float x[K][16];
+    constexpr int NV = V / 16, RPT = K / 16;
+    const int b = blockIdx.x, vt = b % NV, nh = b / NV, n = nh / H, h = nh - (nh / H) * H;
+    if (n >= N) return;
+    const int s0 = soff[n], G = soff[n + 1] - s0;
+    if (G < 3) return;
+    const int tid = threadIdx.x, col = tid & 15, rg = tid >> 4;
+    const size_t kv = static_cast<size_t>(K) * V;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int row = rg * RPT + i;
+        x[row][col] = sb.sin[(static_cast<size_t>(s0 + 1) * H + h) * kv + static_cast<size_t>(row) * V + vt * 16 + col];
+    }
+    for (int gl = 1; gl <= G - 2; ++gl) {
+        const float *mg = sb.mapm + (static_cast<size_t>(s0 + gl) * H + h) * K * K;
+        const float *ng = sb.mapn + (static_cast<size_t>(s0 + gl) * H + h) * kv;
+        for (int p = tid; p < K * K / 4; p += 256) {
+            const float4 v = reinterpret_cast<const float4 *>(mg)[p];
+            const int row = (4 * p) / K, c4 = (4 * p) % K;
+            m[row][c4 + 0] = v.x; m[row][c4 + 1] = v.y; m[row][c4 + 2] = v.z; m[row][c4 + 3] = v.w;
+        }
+        __syncthreads();
+        float y[RPT];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int row = rg * RPT + i;
+            float acc = ng[static_cast<size_t>(row) * V + vt * 16 + col];
+            for (int kk = 0; kk < K; kk += 4) {
+                const float4 mv = *reinterpret_cast<const float4 *>(&m[row][kk]);
+                acc = fmaf(mv.x, x[kk][col], acc);
+                acc = fmaf(mv.y, x[kk + 1][col], acc);
+                acc = fmaf(mv.z, x[kk + 2][col], acc);
+                acc = fmaf(mv.w, x[kk + 3][col], acc);
+            }
+            y[i] = acc;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int row = rg * RPT + i;
+            x[row][col] = y[i];
+            sb.sin[(static_cast<size_t>(s0 + gl + 1) * H + h) * kv + static_cast<size_t>(row) * V + vt * 16 + col] = y[i];
+        }
+        __syncthreads();
+    }
+}
+
+template <int K, int V, typename TOut>
+__global__ __launch_bounds__(256) void out_kernel(PrefillArgs a, const int32_t *off, const int32_t *soff, int L,
+                                                  const char *recs, SegBufs sb) {
+    constexpr int NB = V / 64;
+    __shared__ __attribute__((aligned(16))) char lb0[ScanBuf<K, V>::BYTES];
+    __shared__ __attribute__((aligned(16))) char lb1[ScanBuf<K, V>::BYTES];
+    const int H = a.H;
+    const int s = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+    if (s >= soff[a.N]) return;
+    const SegInfo si = seg_of(soff, a.N, s);
+    const int tid = threadIdx.x, l = tid & 63, r = l & 15, g = l >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col0 = 16 * NB * w;
+    const int cb = off[si.n] + si.gl * L, ce = min(off[si.n + 1], cb + L);
+    const int tbeg = a.cu_seqlens[si.n] + si.gl * L * kC, tend = a.cu_seqlens[si.n + 1];
+    const size_t nkv = (static_cast<size_t>(si.n) * H + h) * K * V;
+    f4 S[NB][K / 16];
+    const float *init = si.G == 1 ? (a.s0 ? a.s0 + nkv : nullptr) : sb.sin + (static_cast<size_t>(s) * H + h) * K * V;
+    load_state<K, NB>(S, init, V, col0, r, g);
+    run_segment<K, V, NB, true, true, TOut>(lb0, lb1, S, recs + static_cast<size_t>(h) * a_nc(a) * Rec<K>::BYTES,
+                                            cb, ce, tbeg, tend, static_cast<const bf16_t *>(a.v),
+                                            static_cast<TOut *>(a.o), H, h, a.scale, tid, w, l, r, g, col0);
+    if (si.gl == si.G - 1 && a.sT) store_state<K, NB>(S, a.sT + nkv, V, col0, r, g);
+}
+
+// Chunks per segment: enough segments to give every compute unit a (segment,
+// head) at this size, and at least 16 chunks each. KDA_SEG_CHUNKS overrides it
+// (tests of the segment bookkeeping at small sizes).
+int seg_chunks(int32_t N, int32_t T, int32_t H) {
+    if (const char *e = std::getenv("KDA_SEG_CHUNKS")) {
+        const int v = std::atoi(e);
+        if (v >= 1) return v;
+    }
+    const int64_t nc = (static_cast<int64_t>(T) + kC - 1) / kC + N;
+    return static_cast<int>(std::max<int64_t>(16, (nc * H + 255) / 256));
+}
+
+template <int K, int V>
+struct WsLayout {
+    int L;
+    size_t nc, nseg, off, soff, recs, sin, mapn, mapm, bytes;
+    WsLayout(int32_t N, int32_t T, int32_t H) {
+        L = seg_chunks(N, T, H);
+        nc = static_cast<size_t>((T + kC - 1) / kC) + N;
+        nseg = (nc + L - 1) / L + N;
+        off = 0;
+        soff = align256(static_cast<size_t>(N + 1) * 4);
+        recs = soff + align256(static_cast<size_t>(N + 1) * 4);
+        sin = recs + nc * H * Rec<K>::BYTES;
+        mapn = sin + nseg * H * K * V * 4;
+        mapm = mapn + nseg * H * K * V * 4;
+        bytes = mapm + nseg * H * K * K * 4;
+    }
+};
 
 template <int K, int V>
 hipError_t launch_kv(const PrefillArgs &a, hipStream_t st) {
-    using R = Rec<K>;
-    const size_t nc_max = a_nc(a);
-    int32_t *off = static_cast<int32_t *>(a.ws);
-    char *recs = static_cast<char *>(a.ws) + align256(static_cast<size_t>(a.N + 1) * 4);
-    hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(256), 0, st, a.cu_seqlens, a.N, off);
+    const WsLayout<K, V> lay(a.N, a.T, a.H);
+    char *ws = static_cast<char *>(a.ws);
+    int32_t *off = reinterpret_cast<int32_t *>(ws + lay.off);
+    int32_t *soff = reinterpret_cast<int32_t *>(ws + lay.soff);
+    char *recs = ws + lay.recs;
+    const SegBufs sb{reinterpret_cast<float *>(ws + lay.sin), reinterpret_cast<float *>(ws + lay.mapm),
+                     reinterpret_cast<float *>(ws + lay.mapn)};
+    hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(256), 0, st, a.cu_seqlens, a.N, lay.L, off, soff);
     if (a.T > 0)
-        hipLaunchKernelGGL((prep_kernel<K>), dim3(static_cast<unsigned>(nc_max * a.H)), dim3(256), 0, st,
-                           a, off, recs);
-    const unsigned units = static_cast<unsigned>(a.N) * a.H;
-    const dim3 grid(((units + 7) / 8) * 8 * (V / 16));
+        hipLaunchKernelGGL((prep_kernel<K>), dim3(static_cast<unsigned>(lay.nc * a.H)), dim3(256), 0, st, a, off,
+                           recs);
+    // every sequence has at most ceil(T / 64) chunks: one segment if that fits in L
+    const int64_t maxc = (static_cast<int64_t>(a.T) + kC - 1) / kC;
+    const size_t units = lay.nseg * a.H;
+    if (maxc > lay.L) {
+        hipLaunchKernelGGL((seg_kernel<K, V>), dim3(static_cast<unsigned>((units + 7) / 8 * 16)), dim3(256), 0, st, a,
+                           off, soff, lay.L, recs, sb);
+        if (maxc > 2 * static_cast<int64_t>(lay.L))
+            hipLaunchKernelGGL((prefix_kernel<K, V>), dim3(static_cast<unsigned>(a.N) * a.H * (V / 16)), dim3(256), 0,
+                               st, soff, a.N, a.H, sb);
+    }
     if (a.out_dtype == KDA_BF16)
-        hipLaunchKernelGGL((scan_kernel<K, V, bf16_t>), grid, dim3(256), 0, st, a, off, recs);
+        hipLaunchKernelGGL((out_kernel<K, V, bf16_t>), dim3(static_cast<unsigned>(units)), dim3(256), 0, st, a, off,
+                           soff, lay.L, recs, sb);
     else
-        hipLaunchKernelGGL((scan_kernel<K, V, float>), grid, dim3(256), 0, st, a, off, recs);
-    (void)sizeof(R);
+        hipLaunchKernelGGL((out_kernel<K, V, float>), dim3(static_cast<unsigned>(units)), dim3(256), 0, st, a, off,
+                           soff, lay.L, recs, sb);
     return hipGetLastError();
-}
-
-template <int K>
-size_t workspace_k(int32_t N, int32_t T, int32_t H) {
-    const size_t nc_max = static_cast<size_t>((T + kC - 1) / kC) + N;
-    return align256(static_cast<size_t>(N + 1) * 4) + nc_max * H * Rec<K>::BYTES;
 }
 
 }  // namespace
 
 size_t prefill_mfma_workspace(int32_t N, int32_t T, int32_t H, int32_t K, int32_t V) {
-    (void)V;
-    return K == 128 ? workspace_k<128>(N, T, H) : workspace_k<64>(N, T, H);
+    if (K == 128 && V == 128) return WsLayout<128, 128>(N, T, H).bytes;
+    if (K == 128 && V == 64) return WsLayout<128, 64>(N, T, H).bytes;
+    if (K == 64 && V == 128) return WsLayout<64, 128>(N, T, H).bytes;
+    return WsLayout<64, 64>(N, T, H).bytes;
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t st) {

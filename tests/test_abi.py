@@ -79,7 +79,18 @@ def test_chunk_fwd_rejects(lib, over, status):
 
 
 def test_workspace_query(lib):
-    assert kda.kda_chunk_fwd_workspace_size(16, 524288, 32, 128, 128, __import__("torch").bfloat16) == 0
+    import torch
+    ws = kda.kda_chunk_fwd_workspace_size
+    # the bf16 path stages one record per (chunk, head): at least 54 KB each at d_k = 128
+    big = ws(16, 524288, 32, 128, 128, torch.bfloat16)
+    assert big >= (524288 // 64) * 32 * 54 * 1024
+    assert ws(1, 0, 4, 128, 128, torch.bfloat16) > 0          # offsets even without tokens
+    assert ws(1, 4096, 4, 128, 128, torch.float32) == 0       # the fp32 path needs none
+    assert ws(1, 4096, 4, 96, 128, torch.bfloat16) == 0       # unsupported head dim
+    assert ws(0, 4096, 4, 128, 128, torch.bfloat16) == 0      # invalid N
+    # grows with the token count and the head count
+    assert ws(1, 8192, 4, 128, 128, torch.bfloat16) > ws(1, 4096, 4, 128, 128, torch.bfloat16)
+    assert ws(1, 4096, 8, 128, 128, torch.bfloat16) > ws(1, 4096, 4, 128, 128, torch.bfloat16)
 
 
 def _decode(lib, **over):

@@ -82,6 +82,28 @@ def test_prefill_null_vs_zero_state_alias_and_determinism():
     assert torch.equal(o4, o5) and torch.equal(s4, st)
 
 
+@pytest.mark.parametrize("seg", ["1", "2", "3"])
+def test_prefill_segmented_state_pass(seg, monkeypatch):
+    """The state pass cut into segments of `seg` chunks (map pass, prefix over
+    segments, output pass) on ragged packed sequences, including empty ones,
+    with a random initial state; final_state aliasing initial_state."""
+    monkeypatch.setenv("KDA_SEG_CHUNKS", seg)
+    inp = inputs.prefill_inputs(11, [0, 700, 64, 1, 389, 0, 200], 3, 128, 128, "bf16", 0.1, "random")
+    d = _prefill_case(inp)
+    o1, s1 = gc.run_prefill(d)
+    st = d["initial_state"].clone()
+    o2, s2 = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"],
+                               d["cu_seqlens"], initial_state=st, final_state=st)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, st)
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64), (64, 64)])
+def test_prefill_segmented_head_dims(dk, dv, monkeypatch):
+    monkeypatch.setenv("KDA_SEG_CHUNKS", "2")
+    _prefill_case(inputs.prefill_inputs(12, [520, 70, 300], 2, dk, dv, "bf16", 0.1, "random"))
+
+
 def test_prefill_long_128k_sampled():
     """One 131072-token sequence, H=32, d=128, bf16, random initial state:
     heads 0 and 31 computed completely by the oracle."""
