@@ -438,11 +438,12 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a, const int32_t 
 //  * prefix_kernel: S_in(g + 1) = M_g S_in(g) + N_g along the middle segments;
 //  * out_kernel, every segment in parallel from its incoming state, with outputs;
 //    the last segment of a sequence writes the final state.
-// A workgroup is four waves over all columns of one (segment, head) state (or of
-// M or N); each wave holds 16 NB columns x d_k rows in MFMA accumulators. A
-// chunk's record is copied global -> LDS once per workgroup with direct-to-LDS
-// loads, one chunk ahead, into a two-buffer ring, so that no record is streamed
-// by more than one compute unit at a time.
+// A workgroup covers all columns of one (segment, head) state (and of M), two
+// waves per SIMD; each wave holds 16 or 32 columns x d_k rows in MFMA
+// accumulators. A chunk's record is copied global -> LDS once per workgroup with
+// direct-to-LDS loads, one chunk ahead, into a two-buffer ring, so that no record
+// is streamed by more than one compute unit at a time; while one wave of a SIMD
+// waits on the memory pipeline the other computes.
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -465,40 +466,87 @@ struct ScanBuf {
     static constexpr int BYTES = VT + VTile<V>::BYTES;
 };
 
-// Copy chunk data into LDS buffer `dst`, spread over the four waves: the record
+// Direct-to-LDS copies (LDS[M0 + inst_offset + size * lane] = global[addr + inst_offset]).
+// They are issued as inline assembly, so the compiler does not see them as LDS
+// stores and does not make reads of the other ring buffer wait for them: every
+// copy is awaited explicitly (vmcnt) before the workgroup barrier that precedes
+// the first read of its buffer. M0 is used by nothing else in these kernels.
+// (readfirstlane returns a signed int: both halves go through uint32_t before
+// widening, so that a low word with bit 31 set is not sign-extended into the high one)
+__device__ __forceinline__ uint32_t sgpr_u32(uint32_t x) {
+    return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(x)));
+}
+__device__ __forceinline__ uint32_t lds_addr(const char *p) {
+    return sgpr_u32(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)p)));
+}
+__device__ __forceinline__ uint64_t uniform_addr(const void *p) {
+    const uint64_t b = reinterpret_cast<uint64_t>(p);
+    return (static_cast<uint64_t>(sgpr_u32(static_cast<uint32_t>(b >> 32))) << 32) |
+           static_cast<uint64_t>(sgpr_u32(static_cast<uint32_t>(b)));
+}
+// (the clobber keeps the compiler from assuming an M0 value across these; the
+// warning only says it will not save and restore M0 around them)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes per lane from uniform base + per-lane 32-bit offset
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff, const char *lds) {
+    __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :
+                     : "s"(lds_addr(lds)), "v"(voff), "s"(uniform_addr(base))
+                     : "memory", "m0");
+}
+// 16 bytes per lane from a per-lane 64-bit address
+__device__ __forceinline__ void dma16v(const void *addr, const char *lds) {
+    __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                     :
+                     : "s"(lds_addr(lds)), "v"(reinterpret_cast<uint64_t>(addr))
+                     : "memory", "m0");
+}
+// 4 bytes per lane, 64 lanes = 256 B, uniform base + 4 lane
+__device__ __forceinline__ void dma4(const void *base, uint32_t voff, const char *lds) {
+    __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                     :
+                     : "s"(lds_addr(lds)), "v"(voff), "s"(uniform_addr(base))
+                     : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Copy chunk data into LDS buffer `dst`, spread over the NW waves: the record
 // fragments the pass reads (all of them with outputs, else K.e^G, its transpose
 // with e^{G_n-G}, and T), e^{G_n} and beta, and (HASV) the 64 x V tile of V.
 // Tokens past the sequence end read the last token (finite; beta is 0 there).
-template <int K, int V, bool FULL, bool HASV>
+template <int K, int V, bool FULL, bool HASV, int NW>
 __device__ __forceinline__ void copy_chunk(char *dst, const char *rec, const bf16_t *vg, int t0, int tend,
                                            int H, int h, int w, int l) {
     using R = Rec<K>;
     constexpr int NKX = 4 * (K / 32);
     constexpr int KG0 = static_cast<int>(R::KGT / 1024);
     constexpr int NF = FULL ? static_cast<int>(R::GAM / 1024) : NKX + 2 * (K / 16) + 6;
-    for (int f = w; f < NF; f += 4) {
+    const uint32_t lo = static_cast<uint32_t>(l) * 16u;
+    for (int f = w; f < NF; f += NW) {
         const int fi = (FULL || f < NKX) ? f : f - NKX + KG0;
-        __builtin_amdgcn_global_load_lds(rec + fi * 1024 + l * 16, (lds_void *)(dst + fi * 1024), 16, 0, 0);
+        dma16(rec + fi * 1024, lo, dst + fi * 1024);
     }
-    // e^{G_n} [K] and beta [64], fp32: K + 64 words, 4 bytes per lane; the instruction
-    // offset applies to both the global and the LDS address
+    // e^{G_n} [K] and beta [64], fp32: K + 64 words in copies of 256 B
     static_assert(R::BET + 4 * kC == R::GAM + 256 * ((K + kC) / 64), "gamma + beta span");
-    if (w == 0) {
-        const char *src = rec + R::GAM + l * 4;
-        __builtin_amdgcn_global_load_lds(src, (lds_void *)(dst + R::GAM), 4, 0, 0);
-        __builtin_amdgcn_global_load_lds(src, (lds_void *)(dst + R::GAM), 4, 256, 0);
-        if (K == 128) __builtin_amdgcn_global_load_lds(src, (lds_void *)(dst + R::GAM), 4, 512, 0);
+    if (w == NW - 1) {
+        const uint32_t l4 = static_cast<uint32_t>(l) * 4u;
+#pragma unroll
+        for (int q = 0; q < (K + kC) / 64; ++q) dma4(rec + R::GAM + q * 256, l4, dst + R::GAM + q * 256);
     }
     if (HASV) {
         using VT = VTile<V>;
         constexpr int LPR = 2 * V / 16;  // lanes per token row
-        for (int q = w; q < VT::NI; q += 4) {
+        for (int q = w; q < VT::NI; q += NW) {
             const int tok = min(t0 + q * VT::RPI + l / LPR, tend - 1);
-            __builtin_amdgcn_global_load_lds(vg + (static_cast<size_t>(tok) * H + h) * V + (l % LPR) * 8,
-                                             (lds_void *)(dst + ScanBuf<K, V>::VT + q * (1024 + kPad)), 16, 0, 0);
+            dma16v(vg + (static_cast<size_t>(tok) * H + h) * V + (l % LPR) * 8,
+                   dst + ScanBuf<K, V>::VT + q * (1024 + kPad));
         }
     }
 }
+
+// fp32 -> bf16 bits, round to nearest even (the gfx950 conversion instruction)
+__device__ __forceinline__ bf16_t bf16_rne(float x) { return __builtin_bit_cast(bf16_t, static_cast<__bf16>(x)); }
 
 __device__ __forceinline__ half8 lds_frag(const char *buf, size_t off, int l) {
     return *reinterpret_cast<const half8 *>(buf + off + l * 16);
@@ -661,21 +709,25 @@ struct ChunkStep {
 };
 
 // The chunks [cb, ce) of one segment (tokens from tbeg; the sequence ends at tend)
-// for the wave's state columns col0 .. col0 + 16 NB - 1. With OUT, the outputs of
-// every chunk go to `og`: bf16 through an LDS tile in the V region of the chunk's
-// buffer (written once all waves have read V, stored by whole rows at the next
-// chunk), fp32 directly from the registers.
-template <int K, int V, int NB, bool OUT, bool HASV, typename TOut>
+// on a workgroup of NW waves. Every wave takes its share of the copies (the V tile
+// when COPYV); an active wave also advances its state columns col0 .. col0 + 16 NB - 1
+// (with V when HASV). With OUT, the outputs of every chunk go to `og`: bf16 through
+// an LDS tile in the V region of the chunk's buffer (written once all waves have
+// read V, stored by whole rows at the next chunk), fp32 directly from the registers.
+template <int K, int V, int NB, bool OUT, bool HASV, bool COPYV, int NW, typename TOut>
 __device__ __forceinline__ void run_segment(char *lb0, char *lb1, f4 (&S)[NB][K / 16], const char *hrec, int cb,
                                             int ce, int tbeg, int tend, const bf16_t *vg, TOut *og, int H, int h,
-                                            float scale, int tid, int w, int l, int r, int g, int col0) {
+                                            float scale, bool active, int tid, int w, int l, int r, int g,
+                                            int col0) {
     constexpr size_t RB = Rec<K>::BYTES;
     constexpr bool TILE = OUT && sizeof(TOut) == 2;
-    constexpr int NP = kC * 2 * V / 16 / 256;  // 16-byte output pieces per thread
+    constexpr int NT = 64 * NW;
+    constexpr int NP = kC * 2 * V / 16 / NT;  // 16-byte output pieces per thread
+    static_assert(!TILE || NP * NT == kC * 2 * V / 16, "output tile pieces");
     using VT = VTile<V>;
     if (cb >= ce) return;
     f4 out[NB][4];
-    copy_chunk<K, V, OUT, HASV>(lb0, hrec + static_cast<size_t>(cb) * RB, vg, tbeg, tend, H, h, w, l);
+    copy_chunk<K, V, OUT, COPYV, NW>(lb0, hrec + static_cast<size_t>(cb) * RB, vg, tbeg, tend, H, h, w, l);
 
     auto body = [&](char *cur, char *oth, int c) {
         const int tc = tbeg + (c - cb) * kC;
@@ -685,27 +737,28 @@ __device__ __forceinline__ void run_segment(char *lb0, char *lb1, f4 (&S)[NB][K 
         if (TILE && c > cb) {
 #pragma unroll
             for (int q = 0; q < NP; ++q) {
-                const int p = q * 256 + tid, row = p / (2 * V / 16), pi = p % (2 * V / 16);
+                const int p = q * NT + tid, row = p / (2 * V / 16), pi = p % (2 * V / 16);
                 pc[q] = *reinterpret_cast<const u4 *>(oth + ScanBuf<K, V>::VT + VT::off(row, pi * 8));
             }
             wait_lds();
         }
         if (TILE) wg_barrier();  // every wave has read the previous output tile out of `oth`
         if (c + 1 < ce)
-            copy_chunk<K, V, OUT, HASV>(oth, hrec + static_cast<size_t>(c + 1) * RB, vg, tc + kC, tend, H, h, w, l);
+            copy_chunk<K, V, OUT, COPYV, NW>(oth, hrec + static_cast<size_t>(c + 1) * RB, vg, tc + kC, tend, H, h, w,
+                                             l);
         if (TILE && c > cb) {
 #pragma unroll
             for (int q = 0; q < NP; ++q) {
-                const int p = q * 256 + tid, row = p / (2 * V / 16), pi = p % (2 * V / 16);
+                const int p = q * NT + tid, row = p / (2 * V / 16), pi = p % (2 * V / 16);
                 const int tok = tc - kC + row;
                 if (tok < tend) *reinterpret_cast<u4 *>(og + (static_cast<size_t>(tok) * H + h) * V + pi * 8) = pc[q];
             }
         }
         ChunkStep<K, V, NB, OUT, HASV> st;
-        st.part_a(cur, S, col0, l, r, g);
+        if (active) st.part_a(cur, S, col0, l, r, g);
         if (TILE) wg_barrier();  // every wave has read V of chunk c: its region takes the outputs
-        st.part_b(cur, S, out, scale, l, g);
-        if (OUT) {
+        if (active) st.part_b(cur, S, out, scale, l, g);
+        if (OUT && active) {
 #pragma unroll
             for (int j = 0; j < NB; ++j)
 #pragma unroll
@@ -715,7 +768,7 @@ __device__ __forceinline__ void run_segment(char *lb0, char *lb1, f4 (&S)[NB][K 
                         const int t = 16 * i + 4 * g + e, col = col0 + 16 * j + r;
                         if (TILE) {
                             *reinterpret_cast<bf16_t *>(cur + ScanBuf<K, V>::VT + VT::off(t, col)) =
-                                f32_to_bf16(out[j][i][e]);
+                                bf16_rne(out[j][i][e]);
                         } else if (tc + t < tend) {
                             io<TOut>::store(og + (static_cast<size_t>(tc + t) * H + h) * V + col, out[j][i][e]);
                         }
@@ -736,7 +789,7 @@ __device__ __forceinline__ void run_segment(char *lb0, char *lb1, f4 (&S)[NB][K 
         const int t0 = tbeg + (ce - 1 - cb) * kC;
 #pragma unroll
         for (int q = 0; q < NP; ++q) {
-            const int p = q * 256 + tid, row = p / (2 * V / 16), pi = p % (2 * V / 16);
+            const int p = q * NT + tid, row = p / (2 * V / 16), pi = p % (2 * V / 16);
             const int tok = t0 + row;
             const u4 v = *reinterpret_cast<const u4 *>(last + ScanBuf<K, V>::VT + VT::off(row, pi * 8));
             if (tok < tend) *reinterpret_cast<u4 *>(og + (static_cast<size_t>(tok) * H + h) * V + pi * 8) = v;
@@ -789,20 +842,22 @@ struct SegBufs {
     float *mapn;  // [segments, H, d_k, d_v] N of middle segments
 };
 
-// blockIdx -> (segment s, head h, part): the two parts (M, N) of a middle segment
-// are 8 blocks apart, so they run on one XCD and share its L2 for the records
+// One workgroup per (segment, head), (d_k + d_v) / 32 waves of 32 columns: the
+// first d_k / 32 waves carry M (from the identity, V = 0) of a middle segment and
+// idle on segment 0; the others carry N (from zero), or on segment 0 the state
+// from the initial state.
 template <int K, int V>
-__global__ __launch_bounds__(256) void seg_kernel(PrefillArgs a, const int32_t *off, const int32_t *soff, int L,
-                                                  const char *recs, SegBufs sb) {
+__global__ __launch_bounds__(64 * (K + V) / 32) void seg_kernel(PrefillArgs a, const int32_t *off,
+                                                                const int32_t *soff, int L, const char *recs,
+                                                                SegBufs sb) {
+    constexpr int NW = (K + V) / 32, WM = K / 32, NB = 2;
     __shared__ __attribute__((aligned(16))) char lb0[ScanBuf<K, V>::BYTES];
     __shared__ __attribute__((aligned(16))) char lb1[ScanBuf<K, V>::BYTES];
-    const int bid = blockIdx.x, q8 = bid >> 3, part = q8 & 1, su = (q8 >> 1) * 8 + (bid & 7);
     const int H = a.H;
-    const int s = su / H, h = su - (su / H) * H;
+    const int s = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
     if (s >= soff[a.N]) return;
     const SegInfo si = seg_of(soff, a.N, s);
     if (si.gl >= si.G - 1) return;    // the last segment has no successor
-    if (si.gl == 0 && part == 1) return;
     const int tid = threadIdx.x, l = tid & 63, r = l & 15, g = l >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int cb = off[si.n] + si.gl * L, ce = min(off[si.n + 1], cb + L);
@@ -810,30 +865,27 @@ __global__ __launch_bounds__(256) void seg_kernel(PrefillArgs a, const int32_t *
     const char *hrec = recs + static_cast<size_t>(h) * a_nc(a) * Rec<K>::BYTES;
     const bf16_t *vg = static_cast<const bf16_t *>(a.v);
     const size_t skv = (static_cast<size_t>(s) * H + h) * K * V;
-    if (si.gl > 0 && part == 0) {
-        constexpr int NB = K / 64;
-        const int col0 = 16 * NB * w;
-        f4 S[NB][K / 16];
+    f4 S[NB][K / 16];
+    if (w < WM) {
+        const int col0 = 32 * w;
 #pragma unroll
         for (int j = 0; j < NB; ++j)
 #pragma unroll
             for (int ct = 0; ct < K / 16; ++ct)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) S[j][ct][e] = (16 * ct + 4 * g + e == col0 + 16 * j + r) ? 1.f : 0.f;
-        run_segment<K, V, NB, false, false, float>(lb0, lb1, S, hrec, cb, ce, tbeg, tend, vg, nullptr, H, h, 1.f,
-                                                   tid, w, l, r, g, col0);
-        store_state<K, NB>(S, sb.mapm + (static_cast<size_t>(s) * H + h) * K * K, K, col0, r, g);
+        run_segment<K, V, NB, false, false, true, NW, float>(lb0, lb1, S, hrec, cb, ce, tbeg, tend, vg, nullptr, H,
+                                                             h, 1.f, si.gl > 0, tid, w, l, r, g, col0);
+        if (si.gl > 0) store_state<K, NB>(S, sb.mapm + (static_cast<size_t>(s) * H + h) * K * K, K, col0, r, g);
     } else {
-        constexpr int NB = V / 64;
-        const int col0 = 16 * NB * w;
-        f4 S[NB][K / 16];
+        const int col0 = 32 * (w - WM);
         const float *init = nullptr;
         if (si.gl == 0 && a.s0) init = a.s0 + (static_cast<size_t>(si.n) * H + h) * K * V;
         load_state<K, NB>(S, init, V, col0, r, g);
         // segment 0: a copy of the initial state for the output pass (final_state may alias it)
         if (si.gl == 0) store_state<K, NB>(S, sb.sin + skv, V, col0, r, g);
-        run_segment<K, V, NB, false, true, float>(lb0, lb1, S, hrec, cb, ce, tbeg, tend, vg, nullptr, H, h, 1.f,
-                                                  tid, w, l, r, g, col0);
+        run_segment<K, V, NB, false, true, true, NW, float>(lb0, lb1, S, hrec, cb, ce, tbeg, tend, vg, nullptr, H, h,
+                                                            1.f, true, tid, w, l, r, g, col0);
         store_state<K, NB>(S, si.gl == 0 ? sb.sin + skv + static_cast<size_t>(H) * K * V : sb.mapn + skv, V, col0, r,
                            g);
     }
@@ -892,9 +944,9 @@ __global__ __launch_bounds__(256) void prefix_kernel(const int32_t *soff, int N,
 }
 
 template <int K, int V, typename TOut>
-__global__ __launch_bounds__(256) void out_kernel(PrefillArgs a, const int32_t *off, const int32_t *soff, int L,
-                                                  const char *recs, SegBufs sb) {
-    constexpr int NB = V / 64;
+__global__ __launch_bounds__(64 * V / 16) void out_kernel(PrefillArgs a, const int32_t *off, const int32_t *soff,
+                                                          int L, const char *recs, SegBufs sb) {
+    constexpr int NB = 1, NW = V / 16;
     __shared__ __attribute__((aligned(16))) char lb0[ScanBuf<K, V>::BYTES];
     __shared__ __attribute__((aligned(16))) char lb1[ScanBuf<K, V>::BYTES];
     const int H = a.H;
@@ -910,9 +962,11 @@ __global__ __launch_bounds__(256) void out_kernel(PrefillArgs a, const int32_t *
     f4 S[NB][K / 16];
     const float *init = si.G == 1 ? (a.s0 ? a.s0 + nkv : nullptr) : sb.sin + (static_cast<size_t>(s) * H + h) * K * V;
     load_state<K, NB>(S, init, V, col0, r, g);
-    run_segment<K, V, NB, true, true, TOut>(lb0, lb1, S, recs + static_cast<size_t>(h) * a_nc(a) * Rec<K>::BYTES,
-                                            cb, ce, tbeg, tend, static_cast<const bf16_t *>(a.v),
-                                            static_cast<TOut *>(a.o), H, h, a.scale, tid, w, l, r, g, col0);
+    run_segment<K, V, NB, true, true, true, NW, TOut>(lb0, lb1, S,
+                                                      recs + static_cast<size_t>(h) * a_nc(a) * Rec<K>::BYTES, cb, ce,
+                                                      tbeg, tend, static_cast<const bf16_t *>(a.v),
+                                                      static_cast<TOut *>(a.o), H, h, a.scale, true, tid, w, l, r, g,
+                                                      col0);
     if (si.gl == si.G - 1 && a.sT) store_state<K, NB>(S, a.sT + nkv, V, col0, r, g);
 }
 
@@ -963,18 +1017,18 @@ hipError_t launch_kv(const PrefillArgs &a, hipStream_t st) {
     const int64_t maxc = (static_cast<int64_t>(a.T) + kC - 1) / kC;
     const size_t units = lay.nseg * a.H;
     if (maxc > lay.L) {
-        hipLaunchKernelGGL((seg_kernel<K, V>), dim3(static_cast<unsigned>((units + 7) / 8 * 16)), dim3(256), 0, st, a,
+        hipLaunchKernelGGL((seg_kernel<K, V>), dim3(static_cast<unsigned>(units)), dim3(64 * (K + V) / 32), 0, st, a,
                            off, soff, lay.L, recs, sb);
         if (maxc > 2 * static_cast<int64_t>(lay.L))
             hipLaunchKernelGGL((prefix_kernel<K, V>), dim3(static_cast<unsigned>(a.N) * a.H * (V / 16)), dim3(256), 0,
                                st, soff, a.N, a.H, sb);
     }
     if (a.out_dtype == KDA_BF16)
-        hipLaunchKernelGGL((out_kernel<K, V, bf16_t>), dim3(static_cast<unsigned>(units)), dim3(256), 0, st, a, off,
-                           soff, lay.L, recs, sb);
+        hipLaunchKernelGGL((out_kernel<K, V, bf16_t>), dim3(static_cast<unsigned>(units)), dim3(64 * V / 16), 0, st, a,
+                           off, soff, lay.L, recs, sb);
     else
-        hipLaunchKernelGGL((out_kernel<K, V, float>), dim3(static_cast<unsigned>(units)), dim3(256), 0, st, a, off,
-                           soff, lay.L, recs, sb);
+        hipLaunchKernelGGL((out_kernel<K, V, float>), dim3(static_cast<unsigned>(units)), dim3(64 * V / 16), 0, st, a,
+                           off, soff, lay.L, recs, sb);
     return hipGetLastError();
 }
 
