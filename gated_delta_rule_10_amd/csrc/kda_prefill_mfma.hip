@@ -163,7 +163,7 @@ template <int K>
 struct PrepSmem {
     static constexpr int NCB = K / 32, LD = 65;
     float tot[4][K];       // decay of each sub-chunk per channel (log, <= 0)
-    float fac[K][16];      // per-channel factors, see prep_kernel
+    float fac[16][K + 4];  // per-channel factors, see prep_kernel
     float beta[kC];
     union {
         struct {
@@ -174,73 +174,112 @@ struct PrepSmem {
             float A[kC][LD];
             float P[kC][LD];
             float T[kC][LD];
-            float X[4][16][17];
         } b;
     } u;
 };
 
-template <int K>
-__global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a, const int32_t *off, char *recs) {
-    constexpr int NCB = K / 32, NCT = K / 16;
-    using R = Rec<K>;
-    __shared__ PrepSmem<K> sm;
-    const int H = a.H;
-    const int c = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
-    if (c >= off[a.N]) return;
+// prep workgroups resident per compute unit (its LDS use allows two)
+constexpr int kPrepWgsPerCu = 2;
+
+// One (chunk, head) work item of prep: chunk c of sequence n, tokens [t0, t0 + nt).
+struct PrepItem {
+    int c, h, n, t0, nt;
+};
+__device__ __forceinline__ PrepItem prep_item(const PrefillArgs &a, const int32_t *off, int u) {
+    const int c = u / a.H, h = u - (u / a.H) * a.H;
     int lo = 0, hi = a.N - 1;  // sequence n with off[n] <= c < off[n + 1]
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (off[mid] <= c) lo = mid; else hi = mid - 1;
     }
-    const int n = lo;
-    const int t0 = a.cu_seqlens[n] + (c - off[n]) * kC;
-    const int nt = min(kC, a.cu_seqlens[n + 1] - t0);
-    char *rec = recs + (static_cast<size_t>(h) * a_nc(a) + c) * R::BYTES;
+    const int t0 = a.cu_seqlens[lo] + (c - off[lo]) * kC;
+    return PrepItem{c, h, lo, t0, min(kC, a.cu_seqlens[lo + 1] - t0)};
+}
 
+// The inputs one lane reads for a work item: token 16w + r of the chunk, channels
+// 32 cb + 16 hf + 4g .. + 3 (bf16 q and k as raw pairs, log decay fp32), and beta.
+template <int K>
+struct PrepRaw {
+    float4 gv[K / 32][2];
+    uint2 kv[K / 32][2], qv[K / 32][2];
+    float beta;
+    bool valid;  // token inside the sequence (else its k, q, decay and beta count as zero)
+
+    // Loads are unconditional: a token past the sequence end reads token t0 of the chunk.
+    __device__ __forceinline__ void load(const PrefillArgs &a, const PrepItem &it, bool ok, int tr, int g) {
+        valid = ok && tr < it.nt;
+        const size_t tok = static_cast<size_t>(it.t0 + (valid ? tr : 0)) * a.H + it.h;
+        const size_t row = tok * K;
+#pragma unroll
+        for (int cb = 0; cb < K / 32; ++cb)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int ch = 32 * cb + 16 * hf + 4 * g;
+                gv[cb][hf] = *reinterpret_cast<const float4 *>(a.g + row + ch);
+                kv[cb][hf] = *reinterpret_cast<const uint2 *>(static_cast<const bf16_t *>(a.k) + row + ch);
+                qv[cb][hf] = *reinterpret_cast<const uint2 *>(static_cast<const bf16_t *>(a.q) + row + ch);
+            }
+        beta = a.beta[tok];
+    }
+    // k, q and the inclusive scan of the log decay over the 16-token sub-chunk
+    // (lanes r of a 16-lane row are its consecutive tokens)
+    __device__ __forceinline__ void unpack(float (&kx)[K / 32][8], float (&qx)[K / 32][8],
+                                           float (&sc)[K / 32][8]) const {
+#pragma unroll
+        for (int cb = 0; cb < K / 32; ++cb)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const float4 gg = valid ? gv[cb][hf] : make_float4(0.f, 0.f, 0.f, 0.f);
+                const uint2 kk = valid ? kv[cb][hf] : make_uint2(0u, 0u);
+                const uint2 qq = valid ? qv[cb][hf] : make_uint2(0u, 0u);
+                sc[cb][4 * hf + 0] = gg.x; sc[cb][4 * hf + 1] = gg.y;
+                sc[cb][4 * hf + 2] = gg.z; sc[cb][4 * hf + 3] = gg.w;
+                kx[cb][4 * hf + 0] = __uint_as_float(kk.x << 16); kx[cb][4 * hf + 1] = __uint_as_float(kk.x & 0xFFFF0000u);
+                kx[cb][4 * hf + 2] = __uint_as_float(kk.y << 16); kx[cb][4 * hf + 3] = __uint_as_float(kk.y & 0xFFFF0000u);
+                qx[cb][4 * hf + 0] = __uint_as_float(qq.x << 16); qx[cb][4 * hf + 1] = __uint_as_float(qq.x & 0xFFFF0000u);
+                qx[cb][4 * hf + 2] = __uint_as_float(qq.y << 16); qx[cb][4 * hf + 3] = __uint_as_float(qq.y & 0xFFFF0000u);
+            }
+#pragma unroll
+        for (int cb = 0; cb < K / 32; ++cb)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float v = sc[cb][e];
+                v += dpp_row_shr<1>(v);
+                v += dpp_row_shr<2>(v);
+                v += dpp_row_shr<4>(v);
+                v += dpp_row_shr<8>(v);
+                sc[cb][e] = v;  // G_r - G_b: log decay from the sub-chunk start to token r (inclusive)
+            }
+    }
+};
+
+// Persistent: each workgroup walks the (chunk, head) items with stride gridDim.x
+// and loads the next item's inputs into registers while it finishes the current
+// one, so the input loads of one item overlap the pairwise products, the UT
+// transform and the stores of the previous one.
+template <int K>
+__global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a, const int32_t *off, char *recs) {
+    constexpr int NCB = K / 32, NCT = K / 16;
+    using R = Rec<K>;
+    __shared__ PrepSmem<K> sm;
+    const int total = off[a.N] * a.H;
     const int tid = threadIdx.x, l = tid & 63, r = l & 15, g = l >> 4;
     // wave index as a scalar: branches on it must be real jumps, because a
     // matrix instruction inside an EXEC-masked block still writes its result
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tr = 16 * w + r;  // token of this lane inside the chunk
-    const bool valid = tr < nt;
-    const size_t row = (static_cast<size_t>(t0 + (valid ? tr : 0)) * H + h) * K;
-    const bf16_t *qp = static_cast<const bf16_t *>(a.q) + row;
-    const bf16_t *kp = static_cast<const bf16_t *>(a.k) + row;
-    const float *gp = a.g + row;
+    int u = blockIdx.x;
+    PrepItem nx = prep_item(a, off, u < total ? u : 0);
+    PrepRaw<K> raw;
+    raw.load(a, nx, u < total, tr, g);
+    for (; u < total; u += gridDim.x) {
+    const PrepItem it = nx;
+    const int c = it.c, h = it.h;
+    char *rec = recs + (static_cast<size_t>(h) * a_nc(a) + c) * R::BYTES;
 
-    // ---- load this lane's 8 channels per 32-channel block, scan the log decay over the sub-chunk
     float kx[NCB][8], qx[NCB][8], s[NCB][8];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const int ch = 32 * cb + 16 * hf + 4 * g;
-            float4 gv = make_float4(0.f, 0.f, 0.f, 0.f), kv = gv, qv = gv;
-            if (valid) {
-                gv = *reinterpret_cast<const float4 *>(gp + ch);
-                kv = io<bf16_t>::load4(kp + ch);
-                qv = io<bf16_t>::load4(qp + ch);
-            }
-            s[cb][4 * hf + 0] = gv.x; s[cb][4 * hf + 1] = gv.y;
-            s[cb][4 * hf + 2] = gv.z; s[cb][4 * hf + 3] = gv.w;
-            kx[cb][4 * hf + 0] = kv.x; kx[cb][4 * hf + 1] = kv.y;
-            kx[cb][4 * hf + 2] = kv.z; kx[cb][4 * hf + 3] = kv.w;
-            qx[cb][4 * hf + 0] = qv.x; qx[cb][4 * hf + 1] = qv.y;
-            qx[cb][4 * hf + 2] = qv.z; qx[cb][4 * hf + 3] = qv.w;
-        }
-    }
-    if (g == 0) sm.beta[tr] = valid ? a.beta[static_cast<size_t>(t0 + tr) * H + h] : 0.f;
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float v = s[cb][e];
-            v += dpp_row_shr<1>(v);
-            v += dpp_row_shr<2>(v);
-            v += dpp_row_shr<4>(v);
-            v += dpp_row_shr<8>(v);
-            s[cb][e] = v;  // G_r - G_b: log decay from the sub-chunk start to token r (inclusive)
-        }
+    raw.unpack(kx, qx, s);
+    if (g == 0) sm.beta[tr] = raw.valid ? raw.beta : 0.f;
     if (r == 15) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
@@ -255,40 +294,58 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a, const int32_t 
     int bad = 0;
     if (tid < K) {
         const float d0 = sm.tot[0][tid], d1 = sm.tot[1][tid], d2 = sm.tot[2][tid], d3 = sm.tot[3][tid];
-        float *f = sm.fac[tid];
+        float f[16];
         f[0] = 1.f; f[1] = __expf(d0); f[2] = __expf(d0 + d1); f[3] = __expf(d0 + d1 + d2);
         f[4] = __expf(d1 + d2 + d3); f[5] = __expf(d2 + d3); f[6] = __expf(d3); f[7] = 1.f;
         f[8] = __expf(fminf(-d0, 80.f)); f[9] = __expf(fminf(-d1, 80.f));
         f[10] = __expf(fminf(-d2, 80.f)); f[11] = __expf(fminf(-d3, 80.f));
         f[12] = __expf(d1); f[13] = __expf(d1 + d2); f[14] = __expf(d2);
         f[15] = __expf(d0 + d1 + d2 + d3);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sm.fac[i][tid] = f[i];
         bad = fmaxf(fmaxf(-d0, -d1), fmaxf(-d2, -d3)) > kFastRange;
     }
     const bool slow = __syncthreads_or(bad);
 
     // ---- elementwise: decayed operands
     half8 kr[NCB], qr[NCB];
+    // this lane's 8 channels of a 32-channel block (chain order) from a per-channel table row
+    auto row8 = [&](const float *rowp, int cb, float (&o)[8]) {
+        const f4 lo4 = *reinterpret_cast<const f4 *>(rowp + 32 * cb + 4 * g);
+        const f4 hi4 = *reinterpret_cast<const f4 *>(rowp + 32 * cb + 16 + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            o[e] = lo4[e];
+            o[4 + e] = hi4[e];
+        }
+    };
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
         half8 kexp, qg, cv0, cv1, cv2, cv3;
+        float tw[8], fb[8], fa[8], fi[8], f2[8], f3[8];
+        row8(sm.tot[w], cb, tw);
+        row8(sm.fac[w], cb, fb);
+        row8(sm.fac[4 + w], cb, fa);
+        row8(sm.fac[8 + w], cb, fi);
+        row8(sm.fac[w == 0 ? 12 : 14], cb, f2);
+        row8(sm.fac[13], cb, f3);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int ch = 32 * cb + kidx(g, e);
-            const float *f = sm.fac[ch];
-            const float rho = __expf(s[cb][e]);                  // e^{G_r - G_b} <= 1
-            const float tau = __expf(sm.tot[w][ch] - s[cb][e]);  // e^{G_{b'} - G_r} <= 1, b' = sub-chunk end
+            const float rho = __expf(s[cb][e]);          // e^{G_r - G_b} <= 1
+            const float tau = __expf(tw[e] - s[cb][e]);  // e^{G_{b'} - G_r} <= 1, b' = sub-chunk end
             const float krv = kx[cb][e] * rho, qrv = qx[cb][e] * rho;
             kr[cb][e] = static_cast<_Float16>(krv);
             qr[cb][e] = static_cast<_Float16>(qrv);
-            kexp[e] = static_cast<_Float16>(krv * f[w]);
-            qg[e] = static_cast<_Float16>(qrv * f[w]);
+            kexp[e] = static_cast<_Float16>(krv * fb[e]);
+            qg[e] = static_cast<_Float16>(qrv * fb[e]);
             const float kt = kx[cb][e] * tau;
-            sm.u.a.kgT[ch][tr] = static_cast<_Float16>(kt * f[4 + w]);
+            sm.u.a.kgT[ch][tr] = static_cast<_Float16>(kt * fa[e]);
             // column operands of column block w for row blocks i = w..3: k_s e^{G_{b_i} - G_s}
-            cv0[e] = static_cast<_Float16>(slow ? 0.f : kt * f[8 + w]);  // i = w (>= 1)
-            cv1[e] = static_cast<_Float16>(kt);                           // i = w + 1
-            cv2[e] = static_cast<_Float16>(kt * (w == 0 ? f[12] : f[14]));  // i = w + 2
-            cv3[e] = static_cast<_Float16>(kt * f[13]);                   // i = 3 (w = 0)
+            cv0[e] = static_cast<_Float16>(slow ? 0.f : kt * fi[e]);  // i = w (>= 1)
+            cv1[e] = static_cast<_Float16>(kt);                         // i = w + 1
+            cv2[e] = static_cast<_Float16>(kt * f2[e]);                 // i = w + 2
+            cv3[e] = static_cast<_Float16>(kt * f3[e]);                 // i = 3 (w = 0)
         }
         *reinterpret_cast<half8 *>(rec + R::KEXP + ((w * NCB + cb) * 64 + l) * 16) = kexp;
         *reinterpret_cast<half8 *>(rec + R::QG + ((w * NCB + cb) * 64 + l) * 16) = qg;
@@ -296,6 +353,12 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a, const int32_t 
         if (w + 1 < 4) sm.u.a.colv[vblk(w + 1, w)][cb][l] = cv1;
         if (w + 2 < 4) sm.u.a.colv[vblk(w + 2, w)][cb][l] = cv2;
         if (w == 0) sm.u.a.colv[vblk(3, 0)][cb][l] = cv3;
+    }
+    // the next item's inputs load from here on (k, q and the decay of this one are no longer held)
+    {
+        const int un = u + static_cast<int>(gridDim.x);
+        nx = prep_item(a, off, un < total ? un : 0);
+        raw.load(a, nx, un < total, tr, g);
     }
     __syncthreads();
 
@@ -325,20 +388,37 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a, const int32_t 
     }
     __syncthreads();  // colv / kgT no longer read; the union now holds A, P, T
 
+    // blocks j <= w of A (strictly lower on the diagonal) and P (lower); the T and P
+    // fragments of even row blocks w also span block w + 1, which must read zero
+    {
+        const f4 bet = *reinterpret_cast<const f4 *>(&sm.beta[16 * w + 4 * g]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j) {
+            if (j > w + 1 || (j == w + 1 && (w & 1))) continue;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int rl = 4 * g + e, rowi = 16 * w + rl, col = 16 * j + r;
-            float av = 0.f, pv = 0.f;
-            if (j < w) { av = accA[j][e]; pv = accP[j][e]; }
-            if (j == w) { av = r < rl ? accA[j][e] : 0.f; pv = r <= rl ? accP[j][e] : 0.f; }
-            sm.u.b.A[rowi][col] = av * sm.beta[rowi];
-            sm.u.b.P[rowi][col] = pv;
-            sm.u.b.T[rowi][col] = 0.f;
+            for (int e = 0; e < 4; ++e) {
+                const int rl = 4 * g + e, rowi = 16 * w + rl, col = 16 * j + r;
+                if (j <= w) {
+                    float av = accA[j][e], pv = accP[j][e];
+                    if (j == w) {
+                        av = r < rl ? av : 0.f;
+                        pv = r <= rl ? pv : 0.f;
+                    }
+                    sm.u.b.A[rowi][col] = av * bet[e];
+                    sm.u.b.P[rowi][col] = pv;
+                } else {
+                    sm.u.b.P[rowi][col] = 0.f;
+                    sm.u.b.T[rowi][col] = 0.f;
+                }
+            }
         }
+    }
     if (slow) {
         // exact diagonal block: e^{G_r - G_s} per element, s <= r inside sub-chunk w
+        // (this item's inputs are read again: the registers now hold the next item's)
+        PrepRaw<K> cr;
+        cr.load(a, it, true, tr, g);
+        cr.unpack(kx, qx, s);
         for (int ss = 0; ss < 16; ++ss) {
             float pa = 0.f, pp = 0.f;
 #pragma unroll
@@ -377,30 +457,24 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a, const int32_t 
         }
     }
     __syncthreads();
-    // blocks below the diagonal: T_wj = -T_ww sum_{m=j}^{w-1} A_wm T_mj, by distance w - j
+    // blocks below the diagonal: T_wj = -T_ww sum_{m=j}^{w-1} A_wm T_mj, by distance w - j,
+    // as fp32 16x16x4 matrix products (lane (r, g): A operand X[r][k], B operand Y[k][r],
+    // result Z[4g + e][r]). X = sum_m A_wm T_mj contracts k = 4s + g in step s; Y = -T_ww X
+    // contracts k = 4g + s in step s, so that X's result registers are Y's B operands.
     for (int lev = 1; lev <= 3; ++lev) {
         const int j = w - lev;
         if (j >= 0) {
-            float x[4] = {0.f, 0.f, 0.f, 0.f};
+            f4 x = zero4();
             for (int m = j; m < w; ++m)
 #pragma unroll
-                for (int kk = 0; kk < 16; ++kk) {
-                    const float tv = sm.u.b.T[16 * m + kk][16 * j + r];
+                for (int s4 = 0; s4 < 4; ++s4)
+                    x = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.u.b.A[16 * w + r][16 * m + 4 * s4 + g],
+                                                             sm.u.b.T[16 * m + 4 * s4 + g][16 * j + r], x, 0, 0, 0);
+            f4 y = zero4();
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) x[e] = fmaf(sm.u.b.A[16 * w + 4 * g + e][16 * m + kk], tv, x[e]);
-                }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sm.u.b.X[w][4 * g + e][r] = x[e];
-        }
-        __syncthreads();
-        if (j >= 0) {
-            float y[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 16; ++kk) {
-                const float xv = sm.u.b.X[w][kk][r];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) y[e] = fmaf(-sm.u.b.T[16 * w + 4 * g + e][16 * w + kk], xv, y[e]);
-            }
+            for (int s4 = 0; s4 < 4; ++s4)
+                y = __builtin_amdgcn_mfma_f32_16x16x4f32(-sm.u.b.T[16 * w + r][16 * w + 4 * g + s4], x[s4], y, 0, 0,
+                                                         0);
 #pragma unroll
             for (int e = 0; e < 4; ++e) sm.u.b.T[16 * w + 4 * g + e][16 * j + r] = y[e];
         }
@@ -422,8 +496,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a, const int32_t 
             *reinterpret_cast<half8 *>(rec + R::PM + (tri(w, ks) * 64 + l) * 16) = pf;
         }
     }
-    if (tid < K) reinterpret_cast<float *>(rec + R::GAM)[tid] = sm.fac[tid][15];
+    if (tid < K) reinterpret_cast<float *>(rec + R::GAM)[tid] = sm.fac[15][tid];
     if (tid < kC) reinterpret_cast<float *>(rec + R::BET)[tid] = sm.beta[tid];
+    __syncthreads();  // the next item rewrites the LDS this one read last
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -970,6 +1046,19 @@ __global__ __launch_bounds__(64 * V / 16) void out_kernel(PrefillArgs a, const i
     if (si.gl == si.G - 1 && a.sT) store_state<K, NB>(S, a.sT + nkv, V, col0, r, g);
 }
 
+// Compute units of the current device (queried once per device).
+int cu_count() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
 // Chunks per segment: enough segments to give every compute unit a (segment,
 // head) at this size, and at least 16 chunks each. KDA_SEG_CHUNKS overrides it
 // (tests of the segment bookkeeping at small sizes).
@@ -1010,9 +1099,11 @@ hipError_t launch_kv(const PrefillArgs &a, hipStream_t st) {
     const SegBufs sb{reinterpret_cast<float *>(ws + lay.sin), reinterpret_cast<float *>(ws + lay.mapm),
                      reinterpret_cast<float *>(ws + lay.mapn)};
     hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(256), 0, st, a.cu_seqlens, a.N, lay.L, off, soff);
-    if (a.T > 0)
-        hipLaunchKernelGGL((prep_kernel<K>), dim3(static_cast<unsigned>(lay.nc * a.H)), dim3(256), 0, st, a, off,
-                           recs);
+    if (a.T > 0) {
+        const size_t items = lay.nc * a.H;
+        const size_t wgs = std::min(items, static_cast<size_t>(kPrepWgsPerCu) * cu_count());
+        hipLaunchKernelGGL((prep_kernel<K>), dim3(static_cast<unsigned>(wgs)), dim3(256), 0, st, a, off, recs);
+    }
     // every sequence has at most ceil(T / 64) chunks: one segment if that fits in L
     const int64_t maxc = (static_cast<int64_t>(a.T) + kC - 1) / kC;
     const size_t units = lay.nseg * a.H;
