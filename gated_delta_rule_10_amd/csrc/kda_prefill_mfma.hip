@@ -785,12 +785,12 @@ struct ChunkStep {
 };
 
 // The chunks [cb, ce) of one segment (tokens from tbeg; the sequence ends at tend)
-// on a workgroup of NW waves. Every wave takes its share of the copies (the V tile
-// when COPYV); an active wave also advances its state columns col0 .. col0 + 16 NB - 1
+// on a workgroup of NW waves. Waves 0 .. CW - 1 issue the copies (the V tile when
+// COPYV); an active wave advances its state columns col0 .. col0 + 16 NB - 1
 // (with V when HASV). With OUT, the outputs of every chunk go to `og`: bf16 through
 // an LDS tile in the V region of the chunk's buffer (written once all waves have
 // read V, stored by whole rows at the next chunk), fp32 directly from the registers.
-template <int K, int V, int NB, bool OUT, bool HASV, bool COPYV, int NW, typename TOut>
+template <int K, int V, int NB, bool OUT, bool HASV, bool COPYV, int NW, int CW, typename TOut>
 __device__ __forceinline__ void run_segment(char *lb0, char *lb1, f4 (&S)[NB][K / 16], const char *hrec, int cb,
                                             int ce, int tbeg, int tend, const bf16_t *vg, TOut *og, int H, int h,
                                             float scale, bool active, int tid, int w, int l, int r, int g,
@@ -803,7 +803,7 @@ __device__ __forceinline__ void run_segment(char *lb0, char *lb1, f4 (&S)[NB][K 
     using VT = VTile<V>;
     if (cb >= ce) return;
     f4 out[NB][4];
-    copy_chunk<K, V, OUT, COPYV, NW>(lb0, hrec + static_cast<size_t>(cb) * RB, vg, tbeg, tend, H, h, w, l);
+    if (w < CW) copy_chunk<K, V, OUT, COPYV, CW>(lb0, hrec + static_cast<size_t>(cb) * RB, vg, tbeg, tend, H, h, w, l);
 
     auto body = [&](char *cur, char *oth, int c) {
         const int tc = tbeg + (c - cb) * kC;
@@ -819,8 +819,8 @@ __device__ __forceinline__ void run_segment(char *lb0, char *lb1, f4 (&S)[NB][K 
             wait_lds();
         }
         if (TILE) wg_barrier();  // every wave has read the previous output tile out of `oth`
-        if (c + 1 < ce)
-            copy_chunk<K, V, OUT, COPYV, NW>(oth, hrec + static_cast<size_t>(c + 1) * RB, vg, tc + kC, tend, H, h, w,
+        if (c + 1 < ce && w < CW)
+            copy_chunk<K, V, OUT, COPYV, CW>(oth, hrec + static_cast<size_t>(c + 1) * RB, vg, tc + kC, tend, H, h, w,
                                              l);
         if (TILE && c > cb) {
 #pragma unroll
@@ -920,8 +920,9 @@ struct SegBufs {
 
 // One workgroup per (segment, head), (d_k + d_v) / 32 waves of 32 columns: the
 // first d_k / 32 waves carry M (from the identity, V = 0) of a middle segment and
-// idle on segment 0; the others carry N (from zero), or on segment 0 the state
-// from the initial state.
+// idle on segment 0, and issue all the chunk copies (their products are the
+// lighter ones); the others carry N (from zero), or on segment 0 the state from
+// the initial state.
 template <int K, int V>
 __global__ __launch_bounds__(64 * (K + V) / 32) void seg_kernel(PrefillArgs a, const int32_t *off,
                                                                 const int32_t *soff, int L, const char *recs,
@@ -950,8 +951,8 @@ __global__ __launch_bounds__(64 * (K + V) / 32) void seg_kernel(PrefillArgs a, c
             for (int ct = 0; ct < K / 16; ++ct)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) S[j][ct][e] = (16 * ct + 4 * g + e == col0 + 16 * j + r) ? 1.f : 0.f;
-        run_segment<K, V, NB, false, false, true, NW, float>(lb0, lb1, S, hrec, cb, ce, tbeg, tend, vg, nullptr, H,
-                                                             h, 1.f, si.gl > 0, tid, w, l, r, g, col0);
+        run_segment<K, V, NB, false, false, true, NW, WM, float>(lb0, lb1, S, hrec, cb, ce, tbeg, tend, vg, nullptr,
+                                                                 H, h, 1.f, si.gl > 0, tid, w, l, r, g, col0);
         if (si.gl > 0) store_state<K, NB>(S, sb.mapm + (static_cast<size_t>(s) * H + h) * K * K, K, col0, r, g);
     } else {
         const int col0 = 32 * (w - WM);
@@ -960,8 +961,8 @@ __global__ __launch_bounds__(64 * (K + V) / 32) void seg_kernel(PrefillArgs a, c
         load_state<K, NB>(S, init, V, col0, r, g);
         // segment 0: a copy of the initial state for the output pass (final_state may alias it)
         if (si.gl == 0) store_state<K, NB>(S, sb.sin + skv, V, col0, r, g);
-        run_segment<K, V, NB, false, true, true, NW, float>(lb0, lb1, S, hrec, cb, ce, tbeg, tend, vg, nullptr, H, h,
-                                                            1.f, true, tid, w, l, r, g, col0);
+        run_segment<K, V, NB, false, true, true, NW, WM, float>(lb0, lb1, S, hrec, cb, ce, tbeg, tend, vg, nullptr, H,
+                                                                h, 1.f, true, tid, w, l, r, g, col0);
         store_state<K, NB>(S, si.gl == 0 ? sb.sin + skv + static_cast<size_t>(H) * K * V : sb.mapn + skv, V, col0, r,
                            g);
     }
@@ -1038,7 +1039,7 @@ __global__ __launch_bounds__(64 * V / 16) void out_kernel(PrefillArgs a, const i
     f4 S[NB][K / 16];
     const float *init = si.G == 1 ? (a.s0 ? a.s0 + nkv : nullptr) : sb.sin + (static_cast<size_t>(s) * H + h) * K * V;
     load_state<K, NB>(S, init, V, col0, r, g);
-    run_segment<K, V, NB, true, true, true, NW, TOut>(lb0, lb1, S,
+    run_segment<K, V, NB, true, true, true, NW, NW, TOut>(lb0, lb1, S,
                                                       recs + static_cast<size_t>(h) * a_nc(a) * Rec<K>::BYTES, cb, ce,
                                                       tbeg, tend, static_cast<const bf16_t *>(a.v),
                                                       static_cast<TOut *>(a.o), H, h, a.scale, true, tid, w, l, r, g,
