@@ -48,6 +48,38 @@ def decode_bytes(B, H, K, V, in_bytes=2, out_bytes=2):
     return B * H * (2 * K * V * 4 + 2 * K * in_bytes + K * 4 + 4 + V * in_bytes + V * out_bytes)
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+SOURCES = ("gated_delta_rule_10_amd/csrc/kda_prefill_mfma.hip", "gated_delta_rule_10_amd/csrc/kda_decode.hip",
+           "gated_delta_rule_10_amd/csrc/kda_api.cpp")
+
+
+def source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(profile):
+    """HBM bytes per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE summary in
+    profiles/<profile>, if it was taken on the kernel sources as they are now
+    (same source hash); None otherwise."""
+    path = os.path.join(ROOT, "profiles", profile)
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    want = source_hash()
+    if f"source sha256 (kda_prefill_mfma.hip, kda_decode.hip, kda_api.cpp): {want}" not in text:
+        return None
+    for line in text.splitlines():
+        if line.startswith("traffic_bytes_per_launch:"):
+            return int(line.split(":")[1])
+    return None
+
+
 def _cpu_threads():
     env = os.environ.get("OMP_NUM_THREADS")
     if env and env.isdigit():
@@ -173,8 +205,9 @@ def main():
                                "chunk 64, o bf16",
                    "global_batch": 1, "seq_len": T, "parallelism": "none (one GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                     "kernel": "kda_chunk_fwd (one launch)",
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic("prefill_long_128k.md"),
+                     "kernel": "kda_chunk_fwd (one call: offsets, prep, map pass, prefix, output pass)",
                      "algorithmic_bytes_per_launch": nbytes},
         "mfma": {"achieved_tflops": round(tflops, 2), "peak_tflops": PEAK_BF16_TFLOPS,
                  "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
@@ -220,6 +253,7 @@ def main():
                         "bf16 q/k/v/o, fresh inputs every step",
             "roofline": {"bound": "hbm", "achieved": round(dgbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(dgbs / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic("decode_b64.md"),
                          "algorithmic_bytes_per_launch": dbytes},
         }
         if cpu_d is not None:

@@ -13,25 +13,24 @@
 //   O  = scale ((Q . e^G) S + P U')
 //   S <- Diag(e^{G_n}) S + (K . e^{G_n-G})^T U'
 //
-// Two kernels.
-//  * prep (one workgroup per chunk and head, all chunks in parallel): every
-//    quantity that does not depend on the state. The 64x64 pairwise matrices
-//    are built from 16-token sub-chunks: for a row in sub-chunk i and a column
-//    in sub-chunk j <= i, e^{G_r-G_s} = e^{G_r-G_b} e^{G_b-G_s} with b the last
-//    token before sub-chunk i, so every factor is <= 1 except, on the diagonal
-//    sub-chunk, e^{G_b-G_s} <= e^{(decay over 16 tokens)}. Those products run
-//    as fp16 16x16x32 MFMAs with fp32 accumulation. Sub-chunks whose decay in
-//    some channel exceeds e^10 over 16 tokens take an exact fp32 per-element
-//    path for their diagonal block instead. T is inverted in fp32 (forward
-//    substitution on the 16x16 diagonal blocks, block recurrence below them).
-//    Results are written to the workspace as fp16 MFMA operand fragments in
-//    exactly the register layout the scan kernel consumes.
-//  * scan (one workgroup per sequence, head and 16 value columns): the
-//    sequential pass over chunks. The state slice lives in MFMA accumulators
-//    (fp32); every value-side operand (state, V - K S, U') is scaled per value
-//    column by a power of two before its fp16 conversion, so the fp16 range
-//    never limits the magnitude of v or of the state. One workgroup barrier per
-//    chunk.
+// Kernels.
+//  * prep (persistent, all (chunk, head) items in parallel): every quantity that
+//    does not depend on the state. The 64x64 pairwise matrices are built from
+//    16-token sub-chunks: for a row in sub-chunk i and a column in sub-chunk
+//    j <= i, e^{G_r-G_s} = e^{G_r-G_b} e^{G_b-G_s} with b the last token before
+//    sub-chunk i, so every factor is <= 1 except, on the diagonal sub-chunk,
+//    e^{G_b-G_s} <= e^{(decay over 16 tokens)}. Those products run as fp16
+//    16x16x32 MFMAs with fp32 accumulation. Sub-chunks whose decay in some
+//    channel exceeds e^10 over 16 tokens take an exact fp32 per-element path
+//    for their diagonal block instead. T is inverted in fp32 (forward
+//    substitution on the 16x16 diagonal blocks, fp32 MFMA block recurrence
+//    below them). Results are written to the workspace as fp16 MFMA operand
+//    fragments in exactly the register layout the state passes consume.
+//  * state passes over segments of consecutive chunks (see below): a map pass,
+//    a prefix over segments and an output pass. The state lives in MFMA
+//    accumulators (fp32); every value-side operand (state, V - K S, U') is
+//    scaled per value column by a power of two before its fp16 conversion, so
+//    the fp16 range never limits the magnitude of v or of the state.
 //
 // MFMA fragment conventions (v_mfma_f32_16x16x32_f16, lane l, r = l % 16,
 // g = l / 16): A operand holds A[r][k(g, e)], B operand B[k(g, e)][r], result
