@@ -39,10 +39,13 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
     const int b = bh / a.H, h = bh - b * a.H;
     const int slot = a.slot_idx ? a.slot_idx[b] : b;
     float *S = a.state + (static_cast<size_t>(slot) * a.H + h) * static_cast<size_t>(K * V);
-    const TIn *qp = static_cast<const TIn *>(a.q) + static_cast<size_t>(bh) * K;
-    const TIn *kp = static_cast<const TIn *>(a.k) + static_cast<size_t>(bh) * K;
+    // value head h reads key head h / (H / Hk)
+    const size_t bhk = static_cast<size_t>(b) * a.Hk + h / (a.H / a.Hk);
+    const TIn *qp = static_cast<const TIn *>(a.q) + bhk * K;
+    const TIn *kp = static_cast<const TIn *>(a.k) + bhk * K;
     const TIn *vp = static_cast<const TIn *>(a.v) + static_cast<size_t>(bh) * V;
     const float *gp = a.g + static_cast<size_t>(bh) * K;
+    const TIn *gxp = static_cast<const TIn *>(a.gx) + static_cast<size_t>(bh) * K;
 
     float4 s[ITERS];
 #pragma unroll
@@ -55,7 +58,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
         const int row = (it * kDecWaves + w) * RPI + rsub;
-        const float al = __expf(gp[row]);
+        const float al = __expf(a.gx ? log_alpha_from(io<TIn>::load(gxp + row), a.gscale) : gp[row]);
         const float kv = io<TIn>::load(kp + row), qv = io<TIn>::load(qp + row);
         s[it] = s[it] * al;
         r4 = fma4(s[it], kv, r4);
@@ -84,10 +87,27 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
         r = r + red_r[ww][c4];
         p = p + red_p[ww][c4];
     }
-    const float4 u = (io<TIn>::load4(vp + c4 * 4) - r) * a.beta[bh];
+    const float bt = a.by ? sigmoid_f(io<TIn>::load(static_cast<const TIn *>(a.by) + bh)) : a.beta[bh];
+    const float4 u = (io<TIn>::load4(vp + c4 * 4) - r) * bt;
+    float4 ov = fma4(u, kq, p) * a.scale;
+    if (a.norm) {  // o / sqrt(mean o^2 + eps) over the LPR lanes of the row (uniform branch)
+        float ss = ov.x * ov.x + ov.y * ov.y + ov.z * ov.z + ov.w * ov.w;
+#pragma unroll
+        for (int m = 1; m < LPR; m <<= 1) ss += __shfl_xor(ss, m);
+        ov = ov * rsqrtf(ss / V + a.eps);
+        if (a.nw) {
+            const float4 wv = io<float>::load4(a.nw + c4 * 4);
+            ov = make_float4(ov.x * wv.x, ov.y * wv.y, ov.z * wv.z, ov.w * wv.w);
+        }
+    }
+    if (a.z) {
+        const float4 zv = io<TIn>::load4(static_cast<const TIn *>(a.z) + static_cast<size_t>(bh) * V + c4 * 4);
+        ov = make_float4(ov.x * out_gate_act(zv.x, a.zact), ov.y * out_gate_act(zv.y, a.zact),
+                         ov.z * out_gate_act(zv.z, a.zact), ov.w * out_gate_act(zv.w, a.zact));
+    }
     if (w == 0 && rsub == 0) {
         TOut *op = static_cast<TOut *>(a.o) + static_cast<size_t>(bh) * V;
-        io<TOut>::store4(op + c4 * 4, fma4(u, kq, p) * a.scale);
+        io<TOut>::store4(op + c4 * 4, ov);
     }
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kda.h"
+
 namespace kda {
 
 using bf16_t = uint16_t;  // raw bfloat16 bit pattern
@@ -48,6 +50,16 @@ template <> struct io<bf16_t> {
         *reinterpret_cast<uint2 *>(p) = w;
     }
 };
+
+// Gate activations of the extended entry points (kda_options_t):
+// log alpha = -scale * softplus(x), softplus(x) = ln(1 + e^x) = max(x, 0) + ln(1 + e^-|x|);
+// beta = sigmoid(y) = 1 / (1 + e^-y).
+__device__ __forceinline__ float log_alpha_from(float x, float scale) {
+    return -scale * (fmaxf(x, 0.f) + __logf(1.f + __expf(-fabsf(x))));
+}
+__device__ __forceinline__ float sigmoid_f(float y) { return 1.f / (1.f + __expf(-y)); }
+// output gate act(z): KDA_ACT_NONE -> z, KDA_ACT_SIGMOID -> sigmoid(z)
+__device__ __forceinline__ float out_gate_act(float z, int act) { return act == KDA_ACT_SIGMOID ? sigmoid_f(z) : z; }
 
 __device__ __forceinline__ float4 operator*(float4 a, float s) {
     return make_float4(a.x * s, a.y * s, a.z * s, a.w * s);

@@ -40,6 +40,7 @@
 // product's result feeds the next product's B operand from registers.
 #include <algorithm>
 #include <cstdlib>
+#include <type_traits>
 
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -197,38 +198,56 @@ __device__ __forceinline__ PrepItem prep_item(const PrefillArgs &a, const int32_
 
 // The inputs one lane reads for a work item: token 16w + r of the chunk, channels
 // 32 cb + 16 hf + 4g .. + 3 (bf16 q and k as raw pairs, log decay fp32), and beta.
-template <int K>
+// With GX the log decay comes from bf16 gate pre-activations (log alpha =
+// -gscale softplus(x)) instead of fp32 log alpha.
+template <int K, bool GX>
 struct PrepRaw {
-    float4 gv[K / 32][2];
+    using GT = typename std::conditional<GX, uint2, float4>::type;
+    GT gv[K / 32][2];
     uint2 kv[K / 32][2], qv[K / 32][2];
     float beta;
     bool valid;  // token inside the sequence (else its k, q, decay and beta count as zero)
 
     // Loads are unconditional: a token past the sequence end reads token t0 of the chunk.
+    // q and k come from key head h / (H / Hk) of the value head h.
     __device__ __forceinline__ void load(const PrefillArgs &a, const PrepItem &it, bool ok, int tr, int g) {
         valid = ok && tr < it.nt;
-        const size_t tok = static_cast<size_t>(it.t0 + (valid ? tr : 0)) * a.H + it.h;
-        const size_t row = tok * K;
+        const size_t t = static_cast<size_t>(it.t0 + (valid ? tr : 0));
+        const size_t tok = t * a.H + it.h;
+        const size_t row = tok * K, rowk = (t * a.Hk + it.h / (a.H / a.Hk)) * K;
 #pragma unroll
         for (int cb = 0; cb < K / 32; ++cb)
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 const int ch = 32 * cb + 16 * hf + 4 * g;
-                gv[cb][hf] = *reinterpret_cast<const float4 *>(a.g + row + ch);
-                kv[cb][hf] = *reinterpret_cast<const uint2 *>(static_cast<const bf16_t *>(a.k) + row + ch);
-                qv[cb][hf] = *reinterpret_cast<const uint2 *>(static_cast<const bf16_t *>(a.q) + row + ch);
+                if constexpr (GX)
+                    gv[cb][hf] = *reinterpret_cast<const uint2 *>(static_cast<const bf16_t *>(a.gx) + row + ch);
+                else
+                    gv[cb][hf] = *reinterpret_cast<const float4 *>(a.g + row + ch);
+                kv[cb][hf] = *reinterpret_cast<const uint2 *>(static_cast<const bf16_t *>(a.k) + rowk + ch);
+                qv[cb][hf] = *reinterpret_cast<const uint2 *>(static_cast<const bf16_t *>(a.q) + rowk + ch);
             }
-        beta = a.beta[tok];
+        beta = a.by ? bf16_to_f32(static_cast<const bf16_t *>(a.by)[tok]) : a.beta[tok];
     }
     // k, q and the inclusive scan of the log decay over the 16-token sub-chunk
     // (lanes r of a 16-lane row are its consecutive tokens)
-    __device__ __forceinline__ void unpack(float (&kx)[K / 32][8], float (&qx)[K / 32][8],
-                                           float (&sc)[K / 32][8]) const {
+    __device__ __forceinline__ void unpack(float (&kx)[K / 32][8], float (&qx)[K / 32][8], float (&sc)[K / 32][8],
+                                           float gscale) const {
 #pragma unroll
         for (int cb = 0; cb < K / 32; ++cb)
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
-                const float4 gg = valid ? gv[cb][hf] : make_float4(0.f, 0.f, 0.f, 0.f);
+                float4 gg;
+                if constexpr (GX) {
+                    const uint2 xx = gv[cb][hf];
+                    gg = make_float4(log_alpha_from(__uint_as_float(xx.x << 16), gscale),
+                                     log_alpha_from(__uint_as_float(xx.x & 0xFFFF0000u), gscale),
+                                     log_alpha_from(__uint_as_float(xx.y << 16), gscale),
+                                     log_alpha_from(__uint_as_float(xx.y & 0xFFFF0000u), gscale));
+                } else {
+                    gg = gv[cb][hf];
+                }
+                if (!valid) gg = make_float4(0.f, 0.f, 0.f, 0.f);
                 const uint2 kk = valid ? kv[cb][hf] : make_uint2(0u, 0u);
                 const uint2 qq = valid ? qv[cb][hf] : make_uint2(0u, 0u);
                 sc[cb][4 * hf + 0] = gg.x; sc[cb][4 * hf + 1] = gg.y;
@@ -256,7 +275,7 @@ struct PrepRaw {
 // and loads the next item's inputs into registers while it finishes the current
 // one, so the input loads of one item overlap the pairwise products, the UT
 // transform and the stores of the previous one.
-template <int K>
+template <int K, bool GX>
 __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a, const int32_t *off, char *recs) {
     constexpr int NCB = K / 32, NCT = K / 16;
     using R = Rec<K>;
@@ -269,7 +288,7 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
     const int tr = 16 * w + r;  // token of this lane inside the chunk
     int u = blockIdx.x;
     PrepItem nx = prep_item(a, off, u < total ? u : 0);
-    PrepRaw<K> raw;
+    PrepRaw<K, GX> raw;
     raw.load(a, nx, u < total, tr, g);
     for (; u < total; u += gridDim.x) {
     const PrepItem it = nx;
@@ -277,8 +296,8 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
     char *rec = recs + (static_cast<size_t>(h) * a_nc(a) + c) * R::BYTES;
 
     float kx[NCB][8], qx[NCB][8], s[NCB][8];
-    raw.unpack(kx, qx, s);
-    if (g == 0) sm.beta[tr] = raw.valid ? raw.beta : 0.f;
+    raw.unpack(kx, qx, s, a.gscale);
+    if (g == 0) sm.beta[tr] = raw.valid ? (a.by ? sigmoid_f(raw.beta) : raw.beta) : 0.f;
     if (r == 15) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
@@ -415,9 +434,9 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
     if (slow) {
         // exact diagonal block: e^{G_r - G_s} per element, s <= r inside sub-chunk w
         // (this item's inputs are read again: the registers now hold the next item's)
-        PrepRaw<K> cr;
+        PrepRaw<K, GX> cr;
         cr.load(a, it, true, tr, g);
-        cr.unpack(kx, qx, s);
+        cr.unpack(kx, qx, s, a.gscale);
         for (int ss = 0; ss < 16; ++ss) {
             float pa = 0.f, pp = 0.f;
 #pragma unroll
@@ -783,55 +802,154 @@ struct ChunkStep {
     }
 };
 
+// Output epilogue (kda_options_t), per token and value head, on the fp32 outputs:
+// o <- o / sqrt(mean o^2 + eps) * weight if norm, then o <- o * act(z) if z.
+struct Epi {
+    const bf16_t *z;
+    const float *nw;
+    float eps;
+    int norm, zact;
+};
+
+// fp32 64 x V output tile in LDS; the 16-column blocks of row t are permuted by
+// XOR with (t / 4) % 4, so the four row groups a wave writes at once hit
+// distinct banks while a 16-column block stays contiguous for the row reads.
+template <int V>
+__device__ __forceinline__ int ftile_off(int row, int col) {
+    return (row * V + (col ^ (16 * ((row >> 2) & 3)))) * 4;
+}
+
 // The chunks [cb, ce) of one segment (tokens from tbeg; the sequence ends at tend)
 // on a workgroup of NW waves. Waves 0 .. CW - 1 issue the copies (the V tile when
 // COPYV); an active wave advances its state columns col0 .. col0 + 16 NB - 1
-// (with V when HASV). With OUT, the outputs of every chunk go to `og`: bf16 through
-// an LDS tile in the V region of the chunk's buffer (written once all waves have
-// read V, stored by whole rows at the next chunk), fp32 directly from the registers.
-template <int K, int V, int NB, bool OUT, bool HASV, bool COPYV, int NW, int CW, typename TOut>
-__device__ __forceinline__ void run_segment(char *lb0, char *lb1, f4 (&S)[NB][K / 16], const char *hrec, int cb,
-                                            int ce, int tbeg, int tend, const bf16_t *vg, TOut *og, int H, int h,
-                                            float scale, bool active, int tid, int w, int l, int r, int g,
-                                            int col0) {
+// (with V when HASV). With OUT, the outputs of every chunk go to `og` through an
+// LDS tile written once all waves have read the chunk's K.e^G, Q.e^G and V, and
+// stored by whole rows at the next chunk: bf16 in the V region of the chunk's
+// buffer; with EPI fp32 (in the K.e^G / Q.e^G region, or in `ftd` when that is
+// too small), normalised and gated on the way out. fp32 outputs without EPI are
+// stored directly from the registers.
+template <int K, int V, int NB, bool OUT, bool HASV, bool COPYV, int NW, int CW, bool EPI, typename TOut>
+__device__ __forceinline__ void run_segment(char *lb0, char *lb1, char *ftd, f4 (&S)[NB][K / 16], const char *hrec,
+                                            int cb, int ce, int tbeg, int tend, const bf16_t *vg, TOut *og, int H,
+                                            int h, float scale, const Epi &ep, bool active, int tid, int w, int l,
+                                            int r, int g, int col0) {
     constexpr size_t RB = Rec<K>::BYTES;
-    constexpr bool TILE = OUT && sizeof(TOut) == 2;
+    constexpr bool TILE = OUT && (EPI || sizeof(TOut) == 2);
     constexpr int NT = 64 * NW;
-    constexpr int NP = kC * 2 * V / 16 / NT;  // 16-byte output pieces per thread
-    static_assert(!TILE || NP * NT == kC * 2 * V / 16, "output tile pieces");
+    constexpr int NP = kC * 2 * V / 16 / NT;  // 16-byte bf16 output pieces per thread
+    constexpr int TPR = V / 16;               // threads per row of the fp32 tile (16 columns each)
+    static_assert(!TILE || EPI || NP * NT == kC * 2 * V / 16, "output tile pieces");
+    static_assert(!EPI || TPR * kC == NT, "one 16-column piece of the fp32 tile per thread");
     using VT = VTile<V>;
     if (cb >= ce) return;
     f4 out[NB][4];
     if (w < CW) copy_chunk<K, V, OUT, COPYV, CW>(lb0, hrec + static_cast<size_t>(cb) * RB, vg, tbeg, tend, H, h, w, l);
 
+    // epilogue: this thread's row and 16 columns of the fp32 tile, its weights, and
+    // the output gate of the chunk whose tile is pending
+    const int erow = tid / TPR, ecol = 16 * (tid % TPR);
+    float ew[16];
+    u4 zq[2] = {u4{0u, 0u, 0u, 0u}, u4{0u, 0u, 0u, 0u}};
+    if (EPI) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) ew[c] = ep.nw ? ep.nw[ecol + c] : 1.f;
+    }
+    auto ftb = [&](char *buf) -> char * { return ftd ? ftd : buf; };
+    auto epi_read = [&](const char *fb, f4 (&x)[4]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x[q] = *reinterpret_cast<const f4 *>(fb + ftile_off<V>(erow, ecol + 4 * q));
+    };
+    auto epi_store = [&](const f4 (&x)[4], int t0) {
+        float v[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[4 * q + e] = x[q][e];
+        if (ep.norm) {
+            float ss = 0.f;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) ss = fmaf(v[c], v[c], ss);
+#pragma unroll
+            for (int m = 1; m < TPR; m <<= 1) ss += __shfl_xor(ss, m);
+            const float inv = rsqrtf(ss / V + ep.eps);
+#pragma unroll
+            for (int c = 0; c < 16; ++c) v[c] *= inv * ew[c];
+        }
+        if (ep.z) {
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                const uint32_t wd = zq[c >> 3][(c >> 1) & 3];
+                v[c] *= out_gate_act(__uint_as_float((c & 1) ? (wd & 0xFFFF0000u) : (wd << 16)), ep.zact);
+            }
+        }
+        const int tok = t0 + erow;
+        if (tok < tend) {
+            TOut *dst = og + (static_cast<size_t>(tok) * H + h) * V + ecol;
+            if constexpr (sizeof(TOut) == 2) {
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    u4 pk;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        pk[e] = static_cast<uint32_t>(bf16_rne(v[8 * q + 2 * e])) |
+                                (static_cast<uint32_t>(bf16_rne(v[8 * q + 2 * e + 1])) << 16);
+                    reinterpret_cast<u4 *>(dst)[q] = pk;
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    reinterpret_cast<f4 *>(dst)[q] = f4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+            }
+        }
+    };
+
     auto body = [&](char *cur, char *oth, int c) {
         const int tc = tbeg + (c - cb) * kC;
         wait_all();  // this wave's copies of chunk c, its stores and its LDS writes are done
         wg_barrier();
-        u4 pc[NP];
+        u4 pc[EPI ? 1 : NP];
+        f4 fx[4];
         if (TILE && c > cb) {
+            if (EPI) {
+                epi_read(ftb(oth), fx);
+            } else {
 #pragma unroll
-            for (int q = 0; q < NP; ++q) {
-                const int p = q * NT + tid, row = p / (2 * V / 16), pi = p % (2 * V / 16);
-                pc[q] = *reinterpret_cast<const u4 *>(oth + ScanBuf<K, V>::VT + VT::off(row, pi * 8));
+                for (int q = 0; q < NP; ++q) {
+                    const int p = q * NT + tid, row = p / (2 * V / 16), pi = p % (2 * V / 16);
+                    pc[q] = *reinterpret_cast<const u4 *>(oth + ScanBuf<K, V>::VT + VT::off(row, pi * 8));
+                }
             }
             wait_lds();
         }
-        if (TILE) wg_barrier();  // every wave has read the previous output tile out of `oth`
+        if (TILE) wg_barrier();  // every wave has read the previous output tile
         if (c + 1 < ce && w < CW)
             copy_chunk<K, V, OUT, COPYV, CW>(oth, hrec + static_cast<size_t>(c + 1) * RB, vg, tc + kC, tend, H, h, w,
                                              l);
         if (TILE && c > cb) {
+            if (EPI) {
+                epi_store(fx, tc - kC);
+            } else {
 #pragma unroll
-            for (int q = 0; q < NP; ++q) {
-                const int p = q * NT + tid, row = p / (2 * V / 16), pi = p % (2 * V / 16);
-                const int tok = tc - kC + row;
-                if (tok < tend) *reinterpret_cast<u4 *>(og + (static_cast<size_t>(tok) * H + h) * V + pi * 8) = pc[q];
+                for (int q = 0; q < NP; ++q) {
+                    const int p = q * NT + tid, row = p / (2 * V / 16), pi = p % (2 * V / 16);
+                    const int tok = tc - kC + row;
+                    if (tok < tend)
+                        *reinterpret_cast<u4 *>(og + (static_cast<size_t>(tok) * H + h) * V + pi * 8) = pc[q];
+                }
+            }
+        }
+        if (EPI && ep.z) {  // output gate of chunk c, used when its tile is stored
+            const int tok = tc + erow;
+            zq[0] = zq[1] = u4{0u, 0u, 0u, 0u};
+            if (tok < tend) {
+                const u4 *zp = reinterpret_cast<const u4 *>(ep.z + (static_cast<size_t>(tok) * H + h) * V + ecol);
+                zq[0] = zp[0];
+                zq[1] = zp[1];
             }
         }
         ChunkStep<K, V, NB, OUT, HASV> st;
         if (active) st.part_a(cur, S, col0, l, r, g);
-        if (TILE) wg_barrier();  // every wave has read V of chunk c: its region takes the outputs
+        if (TILE) wg_barrier();  // every wave has read K.e^G, Q.e^G and V of chunk c: the tile may go there
         if (active) st.part_b(cur, S, out, scale, l, g);
         if (OUT && active) {
 #pragma unroll
@@ -841,7 +959,9 @@ __device__ __forceinline__ void run_segment(char *lb0, char *lb1, f4 (&S)[NB][K 
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int t = 16 * i + 4 * g + e, col = col0 + 16 * j + r;
-                        if (TILE) {
+                        if (EPI) {
+                            *reinterpret_cast<float *>(ftb(cur) + ftile_off<V>(t, col)) = out[j][i][e];
+                        } else if (TILE) {
                             *reinterpret_cast<bf16_t *>(cur + ScanBuf<K, V>::VT + VT::off(t, col)) =
                                 bf16_rne(out[j][i][e]);
                         } else if (tc + t < tend) {
@@ -860,14 +980,20 @@ __device__ __forceinline__ void run_segment(char *lb0, char *lb1, f4 (&S)[NB][K 
     if (TILE) {
         wait_all();
         wg_barrier();
-        const char *last = ((ce - 1 - cb) & 1) ? lb1 : lb0;
+        char *last = ((ce - 1 - cb) & 1) ? lb1 : lb0;
         const int t0 = tbeg + (ce - 1 - cb) * kC;
+        if (EPI) {
+            f4 fx[4];
+            epi_read(ftb(last), fx);
+            epi_store(fx, t0);
+        } else {
 #pragma unroll
-        for (int q = 0; q < NP; ++q) {
-            const int p = q * NT + tid, row = p / (2 * V / 16), pi = p % (2 * V / 16);
-            const int tok = t0 + row;
-            const u4 v = *reinterpret_cast<const u4 *>(last + ScanBuf<K, V>::VT + VT::off(row, pi * 8));
-            if (tok < tend) *reinterpret_cast<u4 *>(og + (static_cast<size_t>(tok) * H + h) * V + pi * 8) = v;
+            for (int q = 0; q < NP; ++q) {
+                const int p = q * NT + tid, row = p / (2 * V / 16), pi = p % (2 * V / 16);
+                const int tok = t0 + row;
+                const u4 v = *reinterpret_cast<const u4 *>(last + ScanBuf<K, V>::VT + VT::off(row, pi * 8));
+                if (tok < tend) *reinterpret_cast<u4 *>(og + (static_cast<size_t>(tok) * H + h) * V + pi * 8) = v;
+            }
         }
     }
 }
@@ -911,6 +1037,17 @@ __device__ __forceinline__ SegInfo seg_of(const int32_t *soff, int N, int s) {
     return SegInfo{lo, s - soff[lo], soff[lo + 1] - soff[lo]};
 }
 
+// initial / final state of sequence n, head h: [N, H, d_k, d_v] arrays, or slot
+// caches when slots are given (a negative slot: zero initial state, no final state)
+__device__ __forceinline__ const float *state_in(const PrefillArgs &a, int n, int h) {
+    const int slot = a.slots ? a.slots[n] : n;
+    return (a.s0 && slot >= 0) ? a.s0 + (static_cast<size_t>(slot) * a.H + h) * a.K * a.V : nullptr;
+}
+__device__ __forceinline__ float *state_out(const PrefillArgs &a, int n, int h) {
+    const int slot = a.slots ? a.slots[n] : n;
+    return (a.sT && slot >= 0) ? a.sT + (static_cast<size_t>(slot) * a.H + h) * a.K * a.V : nullptr;
+}
+
 struct SegBufs {
     float *sin;   // [segments, H, d_k, d_v] incoming state of each segment
     float *mapm;  // [segments, H, d_k, d_k] M of middle segments
@@ -950,18 +1087,19 @@ __global__ __launch_bounds__(64 * (K + V) / 32) void seg_kernel(PrefillArgs a, c
             for (int ct = 0; ct < K / 16; ++ct)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) S[j][ct][e] = (16 * ct + 4 * g + e == col0 + 16 * j + r) ? 1.f : 0.f;
-        run_segment<K, V, NB, false, false, true, NW, WM, float>(lb0, lb1, S, hrec, cb, ce, tbeg, tend, vg, nullptr,
-                                                                 H, h, 1.f, si.gl > 0, tid, w, l, r, g, col0);
+        run_segment<K, V, NB, false, false, true, NW, WM, false, float>(lb0, lb1, nullptr, S, hrec, cb, ce, tbeg,
+                                                                        tend, vg, nullptr, H, h, 1.f, Epi{},
+                                                                        si.gl > 0, tid, w, l, r, g, col0);
         if (si.gl > 0) store_state<K, NB>(S, sb.mapm + (static_cast<size_t>(s) * H + h) * K * K, K, col0, r, g);
     } else {
         const int col0 = 32 * (w - WM);
-        const float *init = nullptr;
-        if (si.gl == 0 && a.s0) init = a.s0 + (static_cast<size_t>(si.n) * H + h) * K * V;
+        const float *init = si.gl == 0 ? state_in(a, si.n, h) : nullptr;
         load_state<K, NB>(S, init, V, col0, r, g);
         // segment 0: a copy of the initial state for the output pass (final_state may alias it)
         if (si.gl == 0) store_state<K, NB>(S, sb.sin + skv, V, col0, r, g);
-        run_segment<K, V, NB, false, true, true, NW, WM, float>(lb0, lb1, S, hrec, cb, ce, tbeg, tend, vg, nullptr, H,
-                                                                h, 1.f, true, tid, w, l, r, g, col0);
+        run_segment<K, V, NB, false, true, true, NW, WM, false, float>(lb0, lb1, nullptr, S, hrec, cb, ce, tbeg, tend,
+                                                                       vg, nullptr, H, h, 1.f, Epi{}, true, tid, w,
+                                                                       l, r, g, col0);
         store_state<K, NB>(S, si.gl == 0 ? sb.sin + skv + static_cast<size_t>(H) * K * V : sb.mapn + skv, V, col0, r,
                            g);
     }
@@ -1019,12 +1157,15 @@ __global__ __launch_bounds__(256) void prefix_kernel(const int32_t *soff, int N,
     }
 }
 
-template <int K, int V, typename TOut>
+template <int K, int V, typename TOut, bool EPI>
 __global__ __launch_bounds__(64 * V / 16) void out_kernel(PrefillArgs a, const int32_t *off, const int32_t *soff,
                                                           int L, const char *recs, SegBufs sb) {
     constexpr int NB = 1, NW = V / 16;
+    // the fp32 epilogue tile goes into the K.e^G / Q.e^G region of a chunk buffer when it fits
+    constexpr bool FTD = EPI && static_cast<size_t>(kC) * V * 4 > Rec<K>::KGT;
     __shared__ __attribute__((aligned(16))) char lb0[ScanBuf<K, V>::BYTES];
     __shared__ __attribute__((aligned(16))) char lb1[ScanBuf<K, V>::BYTES];
+    __shared__ __attribute__((aligned(16))) char ftd[FTD ? kC * V * 4 : 16];
     const int H = a.H;
     const int s = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
     if (s >= soff[a.N]) return;
@@ -1034,16 +1175,17 @@ __global__ __launch_bounds__(64 * V / 16) void out_kernel(PrefillArgs a, const i
     const int col0 = 16 * NB * w;
     const int cb = off[si.n] + si.gl * L, ce = min(off[si.n + 1], cb + L);
     const int tbeg = a.cu_seqlens[si.n] + si.gl * L * kC, tend = a.cu_seqlens[si.n + 1];
-    const size_t nkv = (static_cast<size_t>(si.n) * H + h) * K * V;
     f4 S[NB][K / 16];
-    const float *init = si.G == 1 ? (a.s0 ? a.s0 + nkv : nullptr) : sb.sin + (static_cast<size_t>(s) * H + h) * K * V;
+    const float *init = si.G == 1 ? state_in(a, si.n, h) : sb.sin + (static_cast<size_t>(s) * H + h) * K * V;
     load_state<K, NB>(S, init, V, col0, r, g);
-    run_segment<K, V, NB, true, true, true, NW, NW, TOut>(lb0, lb1, S,
-                                                      recs + static_cast<size_t>(h) * a_nc(a) * Rec<K>::BYTES, cb, ce,
-                                                      tbeg, tend, static_cast<const bf16_t *>(a.v),
-                                                      static_cast<TOut *>(a.o), H, h, a.scale, true, tid, w, l, r, g,
-                                                      col0);
-    if (si.gl == si.G - 1 && a.sT) store_state<K, NB>(S, a.sT + nkv, V, col0, r, g);
+    const Epi ep{static_cast<const bf16_t *>(a.z), a.nw, a.eps, a.norm, a.zact};
+    run_segment<K, V, NB, true, true, true, NW, NW, EPI, TOut>(
+        lb0, lb1, FTD ? ftd : nullptr, S, recs + static_cast<size_t>(h) * a_nc(a) * Rec<K>::BYTES, cb, ce, tbeg, tend,
+        static_cast<const bf16_t *>(a.v), static_cast<TOut *>(a.o), H, h, a.scale, ep, true, tid, w, l, r, g, col0);
+    if (si.gl == si.G - 1) {
+        float *fin = state_out(a, si.n, h);
+        if (fin) store_state<K, NB>(S, fin, V, col0, r, g);
+    }
 }
 
 // Compute units of the current device (queried once per device).
@@ -1102,7 +1244,12 @@ hipError_t launch_kv(const PrefillArgs &a, hipStream_t st) {
     if (a.T > 0) {
         const size_t items = lay.nc * a.H;
         const size_t wgs = std::min(items, static_cast<size_t>(kPrepWgsPerCu) * cu_count());
-        hipLaunchKernelGGL((prep_kernel<K>), dim3(static_cast<unsigned>(wgs)), dim3(256), 0, st, a, off, recs);
+        if (a.gx)
+            hipLaunchKernelGGL((prep_kernel<K, true>), dim3(static_cast<unsigned>(wgs)), dim3(256), 0, st, a, off,
+                               recs);
+        else
+            hipLaunchKernelGGL((prep_kernel<K, false>), dim3(static_cast<unsigned>(wgs)), dim3(256), 0, st, a, off,
+                               recs);
     }
     // every sequence has at most ceil(T / 64) chunks: one segment if that fits in L
     const int64_t maxc = (static_cast<int64_t>(a.T) + kC - 1) / kC;
@@ -1114,12 +1261,15 @@ hipError_t launch_kv(const PrefillArgs &a, hipStream_t st) {
             hipLaunchKernelGGL((prefix_kernel<K, V>), dim3(static_cast<unsigned>(a.N) * a.H * (V / 16)), dim3(256), 0,
                                st, soff, a.N, a.H, sb);
     }
-    if (a.out_dtype == KDA_BF16)
-        hipLaunchKernelGGL((out_kernel<K, V, bf16_t>), dim3(static_cast<unsigned>(units)), dim3(64 * V / 16), 0, st, a,
-                           off, soff, lay.L, recs, sb);
-    else
-        hipLaunchKernelGGL((out_kernel<K, V, float>), dim3(static_cast<unsigned>(units)), dim3(64 * V / 16), 0, st, a,
-                           off, soff, lay.L, recs, sb);
+    const dim3 og(static_cast<unsigned>(units)), ob(64 * V / 16);
+    const bool epi = a.norm || a.z;
+    if (a.out_dtype == KDA_BF16) {
+        if (epi) hipLaunchKernelGGL((out_kernel<K, V, bf16_t, true>), og, ob, 0, st, a, off, soff, lay.L, recs, sb);
+        else hipLaunchKernelGGL((out_kernel<K, V, bf16_t, false>), og, ob, 0, st, a, off, soff, lay.L, recs, sb);
+    } else {
+        if (epi) hipLaunchKernelGGL((out_kernel<K, V, float, true>), og, ob, 0, st, a, off, soff, lay.L, recs, sb);
+        else hipLaunchKernelGGL((out_kernel<K, V, float, false>), og, ob, 0, st, a, off, soff, lay.L, recs, sb);
+    }
     return hipGetLastError();
 }
 

@@ -66,11 +66,17 @@ __global__ __launch_bounds__(kNT) void prefill_valu_kernel(PrefillArgs a) {
     const TIn *kg = static_cast<const TIn *>(a.k);
     const TIn *vg = static_cast<const TIn *>(a.v);
     TOut *og = static_cast<TOut *>(a.o);
-    const size_t sbase = (static_cast<size_t>(n) * H + h) * static_cast<size_t>(K) * V;
+    // states: [N, H, K, V], or with slots a cache [slots, H, K, V] read and written at slot[n]
+    // (a negative slot: zero initial state, final state not written)
+    const int slot = a.slots ? a.slots[n] : n;
+    const size_t sbase = (static_cast<size_t>(slot) * H + h) * static_cast<size_t>(K) * V;
+    const float *s0 = slot >= 0 ? a.s0 : nullptr;
+    float *sT = slot >= 0 ? a.sT : nullptr;
+    const int Hk = a.Hk, hk = h / (H / Hk);  // key head of value head h
 
     for (int idx = tid; idx < K * kVT; idx += kNT) {
         const int i = idx / kVT, c = idx % kVT;
-        sm.S[idx] = a.s0 ? a.s0[sbase + static_cast<size_t>(i) * V + j0 + c] : 0.f;
+        sm.S[idx] = s0 ? s0[sbase + static_cast<size_t>(i) * V + j0 + c] : 0.f;
     }
 
     for (int t0 = tbeg; t0 < tend; t0 += kC) {
@@ -80,16 +86,26 @@ __global__ __launch_bounds__(kNT) void prefill_valu_kernel(PrefillArgs a) {
             const int r = idx / K, i = idx % K;
             const bool ok = r < nt;
             const size_t off = (static_cast<size_t>(t0 + r) * H + h) * K + i;
-            sm.KK[r * KP + i] = ok ? io<TIn>::load(kg + off) : 0.f;
-            sm.QQ[r * KP + i] = ok ? io<TIn>::load(qg + off) : 0.f;
-            sm.G[r * KP + i] = ok ? a.g[off] : 0.f;
+            const size_t offk = (static_cast<size_t>(t0 + r) * Hk + hk) * K + i;
+            sm.KK[r * KP + i] = ok ? io<TIn>::load(kg + offk) : 0.f;
+            sm.QQ[r * KP + i] = ok ? io<TIn>::load(qg + offk) : 0.f;
+            float gv = 0.f;
+            if (ok) gv = a.gx ? log_alpha_from(io<TIn>::load(static_cast<const TIn *>(a.gx) + off), a.gscale) : a.g[off];
+            sm.G[r * KP + i] = gv;
         }
         for (int idx = tid; idx < kC * kVT; idx += kNT) {
             const int r = idx / kVT, c = idx % kVT;
             sm.X[idx] = r < nt ? io<TIn>::load(vg + (static_cast<size_t>(t0 + r) * H + h) * V + j0 + c)
                                : 0.f;
         }
-        if (tid < kC) sm.bet[tid] = tid < nt ? a.beta[static_cast<size_t>(t0 + tid) * H + h] : 0.f;
+        if (tid < kC) {
+            float bv = 0.f;
+            if (tid < nt) {
+                const size_t off = static_cast<size_t>(t0 + tid) * H + h;
+                bv = a.by ? sigmoid_f(io<TIn>::load(static_cast<const TIn *>(a.by) + off)) : a.beta[off];
+            }
+            sm.bet[tid] = bv;
+        }
         __syncthreads();
         if (tid < K) {  // inclusive cumulative sum of log alpha over the chunk
             float acc = 0.f;
@@ -168,12 +184,55 @@ __global__ __launch_bounds__(kNT) void prefill_valu_kernel(PrefillArgs a) {
             sm.S[idx] = acc;
         }
     }
-    if (a.sT) {
+    if (sT) {
         for (int idx = tid; idx < K * kVT; idx += kNT) {
             const int i = idx / kVT, c = idx % kVT;
-            a.sT[sbase + static_cast<size_t>(i) * V + j0 + c] = sm.S[idx];
+            sT[sbase + static_cast<size_t>(i) * V + j0 + c] = sm.S[idx];
         }
     }
+}
+
+// Output epilogue in place, one wave per (token, head) row of V values:
+// o <- o / sqrt(mean o^2 + eps) (* weight), then o <- o * act(z).
+template <int V, typename TIn, typename TOut>
+__global__ __launch_bounds__(256) void epilogue_kernel(PrefillArgs a) {
+    constexpr int PER = V / 64;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
+    if (row >= a.T * a.H) return;
+    TOut *op = static_cast<TOut *>(a.o) + static_cast<size_t>(row) * V;
+    float x[PER];
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        x[e] = io<TOut>::load(op + e * 64 + l);
+        ss += x[e] * x[e];
+    }
+    if (a.norm) {
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) ss += __shfl_xor(ss, m);
+        const float inv = rsqrtf(ss / V + a.eps);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) x[e] *= inv * (a.nw ? a.nw[e * 64 + l] : 1.f);
+    }
+    if (a.z) {
+        const TIn *zp = static_cast<const TIn *>(a.z) + static_cast<size_t>(row) * V;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) x[e] *= out_gate_act(io<TIn>::load(zp + e * 64 + l), a.zact);
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) io<TOut>::store(op + e * 64 + l, x[e]);
+}
+
+template <int V>
+hipError_t launch_epi(const PrefillArgs &a, hipStream_t st) {
+    const dim3 grid((static_cast<unsigned>(a.T) * a.H + 3) / 4), block(256);
+    if (a.in_dtype == KDA_F32)
+        hipLaunchKernelGGL((epilogue_kernel<V, float, float>), grid, block, 0, st, a);
+    else if (a.out_dtype == KDA_BF16)
+        hipLaunchKernelGGL((epilogue_kernel<V, bf16_t, bf16_t>), grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL((epilogue_kernel<V, bf16_t, float>), grid, block, 0, st, a);
+    return hipGetLastError();
 }
 
 template <int K, int V>
@@ -189,6 +248,10 @@ hipError_t launch_kv(const PrefillArgs &a, hipStream_t st) {
 }
 
 }  // namespace
+
+hipError_t launch_epilogue(const PrefillArgs &a, hipStream_t st) {
+    return a.V == 128 ? launch_epi<128>(a, st) : launch_epi<64>(a, st);
+}
 
 hipError_t launch_prefill_valu(const PrefillArgs &a, hipStream_t st) {
     if (a.K == 128 && a.V == 128) return launch_kv<128, 128>(a, st);

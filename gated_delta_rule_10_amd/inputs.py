@@ -177,6 +177,23 @@ def prefill_inputs(seed: int, lengths: Sequence[int], H: int, K: int, V: int,
     return PrefillInputs(q, k, v, log_alpha, beta, cu, s0, in_dtype)
 
 
+def option_inputs(seed: int, T: int, Hk: int, H: int, K: int, V: int, in_dtype: str = "bf16") -> dict:
+    """Inputs of the extended entry points for T tokens (or T decode sequences):
+    q, k [T, Hk, K] (unit rows), v [T, H, V], gate pre-activations gate_x
+    [T, H, K] and beta_y [T, H], output gate out_gate [T, H, V], all ~N(0, 1)
+    and rounded to in_dtype, and an fp32 norm weight [V] ~ 1 + 0.1 N(0, 1)."""
+    rng = np.random.default_rng(seed)
+    rnd = bf16_round if in_dtype == "bf16" else (lambda x: x)
+    q = rnd(_l2_normalise(_normal(rng, (T, Hk, K))))
+    k = rnd(_l2_normalise(_normal(rng, (T, Hk, K))))
+    v = rnd(_normal(rng, (T, H, V)))
+    gate_x = rnd(_normal(rng, (T, H, K)))
+    beta_y = rnd(_normal(rng, (T, H)))
+    out_gate = rnd(_normal(rng, (T, H, V)))
+    norm_weight = (np.float32(1.0) + np.float32(0.1) * _normal(rng, (V,))).astype(np.float32)
+    return dict(q=q, k=k, v=v, gate_x=gate_x, beta_y=beta_y, out_gate=out_gate, norm_weight=norm_weight)
+
+
 def decode_inputs(seed: int, steps: int, B: int, H: int, K: int, V: int,
                   slots: Optional[int] = None, in_dtype: str = "bf16",
                   decay_scale: float = 0.1) -> DecodeInputs:

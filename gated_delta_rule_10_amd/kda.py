@@ -17,7 +17,23 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
 KDA_F32, KDA_BF16 = 0, 1
+KDA_ACT_NONE, KDA_ACT_SIGMOID = 0, 1
 CHUNK_SIZE = 64
+
+
+class KdaOptions(ctypes.Structure):
+    """kda_options_t of include/kda.h (field order and C types as declared there)."""
+    _fields_ = [("num_k_heads", ctypes.c_int32),
+                ("gate_x", ctypes.c_void_p),
+                ("beta_y", ctypes.c_void_p),
+                ("gate_scale", ctypes.c_float),
+                ("norm", ctypes.c_int32),
+                ("norm_eps", ctypes.c_float),
+                ("norm_weight", ctypes.c_void_p),
+                ("out_gate", ctypes.c_void_p),
+                ("out_gate_act", ctypes.c_int),
+                ("state_slots", ctypes.c_void_p),
+                ("num_slots", ctypes.c_int32)]
 
 _lib = None
 
@@ -51,6 +67,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_decode_step.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
                                     ctypes.c_int, ctypes.c_int, f32, P]
     lib.kda_decode_step.restype = ctypes.c_int
+    opt = ctypes.POINTER(KdaOptions)
+    lib.kda_chunk_fwd_ex.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, ctypes.c_int,
+                                     ctypes.c_int, f32, P, P, P, i32, P, sz, opt, P]
+    lib.kda_chunk_fwd_ex.restype = ctypes.c_int
+    lib.kda_decode_step_ex.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                       ctypes.c_int, ctypes.c_int, f32, opt, P]
+    lib.kda_decode_step_ex.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -186,4 +209,162 @@ def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                              float(scale), _stream(stream))
     if st != KDA_OK:
         raise KDAError(st, "kda_decode_step")
+    return o
+
+
+def _act_code(act) -> int:
+    if act in (None, "none", KDA_ACT_NONE):
+        return KDA_ACT_NONE
+    if act in ("sigmoid", KDA_ACT_SIGMOID):
+        return KDA_ACT_SIGMOID
+    raise ValueError(f"unknown output gate activation {act!r}")
+
+
+def _options(H, num_k_heads=None, gate_x=None, beta_y=None, gate_scale=1.0, norm=False,
+             norm_eps=1e-6, norm_weight=None, out_gate=None, out_gate_act="none",
+             state_slots=None, num_slots=0) -> KdaOptions:
+    op = KdaOptions()
+    op.num_k_heads = int(num_k_heads or H)
+    for name, t in (("gate_x", gate_x), ("beta_y", beta_y), ("norm_weight", norm_weight),
+                    ("out_gate", out_gate), ("state_slots", state_slots)):
+        if t is not None:
+            _dev(t, name)
+    op.gate_x = None if gate_x is None else gate_x.data_ptr()
+    op.beta_y = None if beta_y is None else beta_y.data_ptr()
+    op.gate_scale = float(gate_scale)
+    op.norm = int(bool(norm))
+    op.norm_eps = float(norm_eps)
+    op.norm_weight = None if norm_weight is None else norm_weight.data_ptr()
+    op.out_gate = None if out_gate is None else out_gate.data_ptr()
+    op.out_gate_act = _act_code(out_gate_act)
+    op.state_slots = None if state_slots is None else state_slots.data_ptr()
+    op.num_slots = int(num_slots)
+    return op
+
+
+def kda_chunk_fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor, *,
+                     log_alpha: Optional[torch.Tensor] = None, beta: Optional[torch.Tensor] = None,
+                     gate_x: Optional[torch.Tensor] = None, beta_y: Optional[torch.Tensor] = None,
+                     gate_scale: float = 1.0, norm: bool = False, norm_eps: float = 1e-6,
+                     norm_weight: Optional[torch.Tensor] = None, out_gate: Optional[torch.Tensor] = None,
+                     out_gate_act="none", state_slots: Optional[torch.Tensor] = None,
+                     scale: float = 1.0, initial_state: Optional[torch.Tensor] = None,
+                     output_final_state: bool = True, final_state: Optional[torch.Tensor] = None,
+                     out_dtype: Optional[torch.dtype] = None, o: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None,
+                     stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """kda_chunk_fwd_ex of include/kda.h.
+
+    q, k: [T, Hk, d_k]; v: [T, H, d_v] with H a multiple of Hk (value head h uses key
+    head h // (H // Hk)); gates either log_alpha [T, H, d_k] fp32 and beta [T, H] fp32,
+    or gate_x [T, H, d_k] / beta_y [T, H] in the input dtype (log_alpha =
+    -gate_scale * softplus(gate_x), beta = sigmoid(beta_y)). Epilogue: norm (RMS over
+    d_v, times norm_weight [d_v] fp32), then out_gate [T, H, d_v] (act "none" or
+    "sigmoid"). With state_slots [N] int32, initial_state is a cache [slots, H, d_k, d_v]
+    and final_state defaults to that same cache (updated in place).
+    Returns (o [T, H, d_v], final_state).
+    """
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("cu_seqlens", cu_seqlens)):
+        _dev(t, name)
+    T, Hk, d_k = q.shape
+    H, d_v = v.shape[1], v.shape[2]
+    N = cu_seqlens.shape[0] - 1
+    if k.shape != q.shape or v.shape[0] != T or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("inconsistent q/k/v shapes or dtypes")
+    if cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    for name, t, shape, dt in (("log_alpha", log_alpha, (T, H, d_k), torch.float32),
+                               ("beta", beta, (T, H), torch.float32),
+                               ("gate_x", gate_x, (T, H, d_k), q.dtype),
+                               ("beta_y", beta_y, (T, H), q.dtype),
+                               ("out_gate", out_gate, (T, H, d_v), q.dtype),
+                               ("norm_weight", norm_weight, (d_v,), torch.float32)):
+        if t is not None:
+            _dev(t, name)
+            if tuple(t.shape) != shape or t.dtype != dt:
+                raise ValueError(f"{name} must be {dt} {shape}")
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((T, H, d_v), dtype=out_dtype, device=q.device)
+    _dev(o, "o")
+    num_slots = 0
+    if state_slots is not None:
+        _dev(state_slots, "state_slots")
+        if state_slots.dtype != torch.int32 or state_slots.shape != (N,):
+            raise ValueError("state_slots must be int32 [N]")
+        if initial_state is None:
+            raise ValueError("state_slots needs the state cache as initial_state")
+        num_slots = initial_state.shape[0]
+        if final_state is None and output_final_state:
+            final_state = initial_state
+    else:
+        if final_state is None and output_final_state:
+            final_state = torch.empty((N, H, d_k, d_v), dtype=torch.float32, device=q.device)
+    for name, t in (("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None:
+            _dev(t, name)
+            if t.dtype != torch.float32 or tuple(t.shape[1:]) != (H, d_k, d_v) or \
+                    (state_slots is None and t.shape[0] != N):
+                raise ValueError(f"{name} must be float32 [{'slots' if state_slots is not None else 'N'}, H, d_k, d_v]")
+    op = _options(H, Hk, gate_x, beta_y, gate_scale, norm, norm_eps, norm_weight, out_gate, out_gate_act,
+                  state_slots, num_slots)
+    if workspace is None:
+        need = int(lib.kda_chunk_fwd_workspace_size(N, T, H, d_k, d_v, _code(q.dtype)))
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.kda_chunk_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(cu_seqlens),
+                              N, T, H, d_k, d_v, _code(q.dtype), _code(out_dtype), float(scale),
+                              _ptr(initial_state), _ptr(final_state), _ptr(o), CHUNK_SIZE,
+                              _ptr(workspace), ws_bytes, ctypes.byref(op), _stream(stream))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_chunk_fwd_ex")
+    return o, final_state
+
+
+def kda_decode_step_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state_cache: torch.Tensor,
+                       slot_idx: Optional[torch.Tensor] = None, *,
+                       log_alpha: Optional[torch.Tensor] = None, beta: Optional[torch.Tensor] = None,
+                       gate_x: Optional[torch.Tensor] = None, beta_y: Optional[torch.Tensor] = None,
+                       gate_scale: float = 1.0, norm: bool = False, norm_eps: float = 1e-6,
+                       norm_weight: Optional[torch.Tensor] = None, out_gate: Optional[torch.Tensor] = None,
+                       out_gate_act="none", scale: float = 1.0, out_dtype: Optional[torch.dtype] = None,
+                       o: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """kda_decode_step_ex of include/kda.h: q, k [B, Hk, d_k]; v [B, H, d_v]; the other
+    options as for kda_chunk_fwd_ex. Returns o [B, H, d_v]."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("state_cache", state_cache)):
+        _dev(t, name)
+    B, Hk, d_k = q.shape
+    H, d_v = v.shape[1], v.shape[2]
+    if k.shape != q.shape or v.shape[0] != B or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("inconsistent q/k/v shapes or dtypes")
+    if state_cache.dtype != torch.float32 or tuple(state_cache.shape[1:]) != (H, d_k, d_v):
+        raise ValueError("state_cache must be float32 [slots, H, d_k, d_v]")
+    for name, t, shape, dt in (("log_alpha", log_alpha, (B, H, d_k), torch.float32),
+                               ("beta", beta, (B, H), torch.float32),
+                               ("gate_x", gate_x, (B, H, d_k), q.dtype),
+                               ("beta_y", beta_y, (B, H), q.dtype),
+                               ("out_gate", out_gate, (B, H, d_v), q.dtype),
+                               ("norm_weight", norm_weight, (d_v,), torch.float32)):
+        if t is not None:
+            _dev(t, name)
+            if tuple(t.shape) != shape or t.dtype != dt:
+                raise ValueError(f"{name} must be {dt} {shape}")
+    if slot_idx is not None:
+        _dev(slot_idx, "slot_idx")
+        if slot_idx.dtype != torch.int32 or slot_idx.shape != (B,):
+            raise ValueError("slot_idx must be int32 [B]")
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((B, H, d_v), dtype=out_dtype, device=q.device)
+    _dev(o, "o")
+    op = _options(H, Hk, gate_x, beta_y, gate_scale, norm, norm_eps, norm_weight, out_gate, out_gate_act)
+    st = lib.kda_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(state_cache),
+                                _ptr(slot_idx), _ptr(o), B, H, d_k, d_v, state_cache.shape[0],
+                                _code(q.dtype), _code(out_dtype), float(scale), ctypes.byref(op),
+                                _stream(stream))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_decode_step_ex")
     return o

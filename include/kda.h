@@ -146,6 +146,91 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v,
                              kda_dtype_t in_dtype, kda_dtype_t out_dtype,
                              float scale, hipStream_t stream);
 
+/*
+ * Extended entry points: the steps just before and just after the operator,
+ * and the serving layout of the states. `opt` may be NULL; a zero-filled
+ * kda_options_t (or NULL) gives exactly kda_chunk_fwd / kda_decode_step.
+ *
+ * Sources: the 2025 attention/MoE review (lanjinlin.com.cn), section
+ * "GatedDeltaNet解读": the gates g and beta are produced from two inputs (a, b),
+ * the key/query heads serve groups of value heads, and the read-out is
+ * RMS-normalised and multiplied by an output gate z; its MiniMax section fuses
+ * the group RMS norm, the sigmoid gate and the product into one kernel.
+ * "线性注意力机制Kimi Linear架构解析与优化实践" (coreui.cn), section 3.2: the
+ * recurrent states kept in one contiguous cache indexed per sequence.
+ * The pages do not give KDA's gate activation; this library uses
+ *     log_alpha = -gate_scale * softplus(gate_x),  beta = sigmoid(beta_y),
+ * with softplus(x) = ln(1 + e^x) and sigmoid(y) = 1 / (1 + e^-y).
+ */
+typedef enum {
+    KDA_ACT_NONE = 0,    /* o <- o * z */
+    KDA_ACT_SIGMOID = 1  /* o <- o * sigmoid(z) */
+} kda_act_t;
+
+typedef struct {
+    /* Grouped value heads: q and k have num_k_heads heads ([*, num_k_heads,
+     * d_k]); value head h uses key head h / (H / num_k_heads). H must be a
+     * multiple of num_k_heads. 0 means H (no grouping). */
+    int32_t num_k_heads;
+    /* Gate pre-activations, in_dtype. gate_x [*, H, d_k] replaces log_alpha
+     * (which must then be NULL); beta_y [*, H] replaces beta (which must then
+     * be NULL). gate_scale > 0 and finite when gate_x is set. */
+    const void *gate_x;
+    const void *beta_y;
+    float gate_scale;
+    /* Output epilogue, per token and value head, in fp32 before the output
+     * rounding: if norm != 0, o <- o / sqrt(mean_j o_j^2 + norm_eps), then
+     * times norm_weight [d_v] (fp32, NULL = 1); then, if out_gate
+     * ([*, H, d_v], in_dtype) is set, o <- o * act(out_gate). norm_eps >= 0. */
+    int32_t norm;
+    float norm_eps;
+    const float *norm_weight;
+    const void *out_gate;
+    kda_act_t out_gate_act;
+    /* Prefill only: states in a slot cache. With state_slots ([N] int32,
+     * device) set, initial_state and final_state are caches
+     * [num_slots, H, d_k, d_v] (usually the same pointer): sequence n starts
+     * from slot state_slots[n] of initial_state and writes its final state to
+     * the same slot of final_state. A negative slot marks padding: the
+     * sequence starts from zeros and its final state is not written. Slots of
+     * different sequences must differ. num_slots >= 1. */
+    const int32_t *state_slots;
+    int32_t num_slots;
+} kda_options_t;
+
+/*
+ * kda_chunk_fwd with options. H is the number of value heads (the heads of
+ * v, log_alpha / gate_x, beta / beta_y, o and the states); the workspace is
+ * kda_chunk_fwd_workspace_size(N, T_total, H, d_k, d_v, in_dtype).
+ * Every option is available for both input types (on the fp32 path the
+ * epilogue runs as a second pass over o). Errors as for kda_chunk_fwd, plus
+ * KDA_ERR_INVALID_ARG for inconsistent options; kda_chunk_fwd itself returns
+ * KDA_ERR_INVALID_ARG when log_alpha or beta is NULL and T_total > 0.
+ */
+kda_status_t kda_chunk_fwd_ex(const void *q, const void *k, const void *v,
+                              const float *log_alpha, const float *beta,
+                              const int32_t *cu_seqlens, int32_t N,
+                              int32_t T_total, int32_t H, int32_t d_k,
+                              int32_t d_v, kda_dtype_t in_dtype,
+                              kda_dtype_t out_dtype, float scale,
+                              const float *initial_state, float *final_state,
+                              void *o, int32_t chunk_size, void *workspace,
+                              size_t workspace_bytes, const kda_options_t *opt,
+                              hipStream_t stream);
+
+/*
+ * kda_decode_step with options (state_slots and num_slots of `opt` are not
+ * used: decode has slot_idx). H is the number of value heads.
+ */
+kda_status_t kda_decode_step_ex(const void *q, const void *k, const void *v,
+                                const float *log_alpha, const float *beta,
+                                float *state_cache, const int32_t *slot_idx,
+                                void *o, int32_t B, int32_t H, int32_t d_k,
+                                int32_t d_v, int32_t num_slots,
+                                kda_dtype_t in_dtype, kda_dtype_t out_dtype,
+                                float scale, const kda_options_t *opt,
+                                hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

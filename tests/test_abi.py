@@ -32,7 +32,27 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_size",
-        "kda_chunk_fwd", "kda_decode_step"])
+        "kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_ex", "kda_decode_step_ex"])
+
+
+def test_options_struct_layout_matches_the_header(tmp_path):
+    """kda_options_t as laid out by a C compiler equals the binding's ctypes mirror."""
+    import subprocess
+    fields = [f for f, _ in kda.KdaOptions._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "kda.h"\nint main(void) {\n'
+                   '  printf("%zu\\n", sizeof(kda_options_t));\n'
+                   + "".join(f'  printf("%zu\\n", offsetof(kda_options_t, {f}));\n' for f in fields)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    try:
+        subprocess.check_call(["gcc", "-std=c99", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                               "-I", "/opt/rocm/include", str(src), "-o", str(exe)])
+    except (OSError, subprocess.CalledProcessError):
+        pytest.skip("no C compiler / ROCm headers for the layout probe")
+    got = [int(x) for x in subprocess.check_output([str(exe)]).split()]
+    assert got[0] == ctypes.sizeof(kda.KdaOptions)
+    assert got[1:] == [getattr(kda.KdaOptions, f).offset for f in fields]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -91,6 +111,42 @@ def test_workspace_query(lib):
     # grows with the token count and the head count
     assert ws(1, 8192, 4, 128, 128, torch.bfloat16) > ws(1, 4096, 4, 128, 128, torch.bfloat16)
     assert ws(1, 4096, 8, 128, 128, torch.bfloat16) > ws(1, 4096, 4, 128, 128, torch.bfloat16)
+
+
+def _prefill_ex(lib, opt, **over):
+    args = dict(q=A, k=A, v=A, g=A, b=A, cu=A, N=2, T=100, H=4, dk=128, dv=128,
+                din=kda.KDA_BF16, dout=kda.KDA_BF16, scale=1.0, s0=None, sT=None, o=A,
+                chunk=64, ws=None, wsb=0)
+    args.update(over)
+    return lib.kda_chunk_fwd_ex(args["q"], args["k"], args["v"], args["g"], args["b"],
+                                args["cu"], args["N"], args["T"], args["H"], args["dk"],
+                                args["dv"], args["din"], args["dout"], args["scale"],
+                                args["s0"], args["sT"], args["o"], args["chunk"], args["ws"],
+                                args["wsb"], ctypes.byref(opt), None)
+
+
+@pytest.mark.parametrize("opt_over,call_over", [
+    (dict(num_k_heads=3), {}),                          # 4 value heads are not a multiple of 3
+    (dict(num_k_heads=-1), {}),
+    (dict(gate_x=A), {}),                               # both gate forms given
+    (dict(gate_x=A, gate_scale=0.0), dict(g=None)),     # gate scale must be positive
+    (dict(beta_y=A), {}),
+    ({}, dict(g=None)),                                 # no gate at all
+    (dict(out_gate=A, out_gate_act=7), {}),
+    (dict(norm=1, norm_eps=-1.0), {}),
+    (dict(norm_weight=A + 4, norm=1), {}),              # misaligned
+    (dict(state_slots=A, num_slots=0), {}),
+])
+def test_chunk_fwd_ex_rejects_inconsistent_options(lib, opt_over, call_over):
+    opt = kda.KdaOptions()
+    for f, val in opt_over.items():
+        setattr(opt, f, val)
+    assert _prefill_ex(lib, opt, **call_over) == kda.KDA_ERR_INVALID_ARG
+
+
+def test_plain_entry_point_needs_both_gates(lib):
+    assert _prefill(lib, g=None) == kda.KDA_ERR_INVALID_ARG
+    assert _decode(lib, b=None) == kda.KDA_ERR_INVALID_ARG
 
 
 def _decode(lib, **over):

@@ -1,0 +1,139 @@
+"""GPU parity of the extended entry points (kda_chunk_fwd_ex, kda_decode_step_ex)
+against the fp64 oracle with the same options (oracle/options.py): grouped
+key heads, gate pre-activations, the RMS-norm / output-gate epilogue and
+slot-indexed states, alone and together, on both input types."""
+
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_10_amd import inputs, kda
+from oracle import options as oo
+from tests import gpu_common as gc
+
+pytestmark = pytest.mark.gpu
+
+
+def _t(x, bf):
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if bf:
+        t = torch.from_numpy(inputs.bf16_bits(x)).view(torch.bfloat16)
+    return t.cuda()
+
+
+def _prefill_case(seed, lens, Hk, H, K, V, dt, *, gates="pre", norm=False, z_act=None,
+                  slots=None, out_dtypes=None, decay=0.1):
+    bf = dt == "bf16"
+    T = int(sum(lens))
+    x = inputs.option_inputs(seed, T, Hk, H, K, V, dt)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    N = len(lens)
+    rng = np.random.default_rng(seed + 1000)
+    kw_o, kw_g = {}, {}
+    if gates == "pre":
+        kw_o.update(gate_x=x["gate_x"], beta_y=x["beta_y"], gate_scale=decay)
+        kw_g.update(gate_x=_t(x["gate_x"], bf), beta_y=_t(x["beta_y"], bf), gate_scale=decay)
+    else:
+        g = (-decay * oo.softplus(x["gate_x"])).astype(np.float32)
+        b = oo.sigmoid(x["beta_y"]).astype(np.float32)
+        kw_o.update(log_alpha=g, beta=b)
+        kw_g.update(log_alpha=_t(g, False), beta=_t(b, False))
+    if norm:
+        kw_o.update(norm=True, norm_eps=1e-5, norm_weight=x["norm_weight"])
+        kw_g.update(norm=True, norm_eps=1e-5, norm_weight=_t(x["norm_weight"], False))
+    if z_act is not None:
+        kw_o.update(out_gate=x["out_gate"], out_gate_act=z_act)
+        kw_g.update(out_gate=_t(x["out_gate"], bf), out_gate_act=z_act)
+    if slots is not None:
+        nslots = max(max(slots) + 2, N)
+        cache = (0.02 * rng.standard_normal((nslots, H, K, V))).astype(np.float32)
+        s_np = np.asarray(slots, np.int32)
+        ref_o, ref_s = oo.prefill_ex(x["q"], x["k"], x["v"], cu, state_slots=s_np, initial_state=cache,
+                                     **kw_o)
+    else:
+        s0 = (0.02 * rng.standard_normal((N, H, K, V))).astype(np.float32)
+        ref_o, ref_s = oo.prefill_ex(x["q"], x["k"], x["v"], cu, initial_state=s0, **kw_o)
+    tol = gc.TOL_BF16 if bf else gc.TOL_F32
+    for od in (out_dtypes or ([torch.bfloat16, torch.float32] if bf else [torch.float32])):
+        if slots is not None:
+            st = torch.from_numpy(cache).cuda()
+            o, sT = kda.kda_chunk_fwd_ex(_t(x["q"], bf), _t(x["k"], bf), _t(x["v"], bf), torch.from_numpy(cu).cuda(),
+                                         state_slots=torch.from_numpy(s_np).cuda(), initial_state=st,
+                                         out_dtype=od, **kw_g)
+        else:
+            o, sT = kda.kda_chunk_fwd_ex(_t(x["q"], bf), _t(x["k"], bf), _t(x["v"], bf), torch.from_numpy(cu).cuda(),
+                                         initial_state=torch.from_numpy(s0).cuda(), out_dtype=od, **kw_g)
+        torch.cuda.synchronize()
+        gc.assert_close(f"o[{od}]", gc.host(o), ref_o, tol, bf16_rounded=od == torch.bfloat16)
+        gc.assert_close("final_state", gc.host(sT), ref_s, tol)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("Hk", [1, 2])
+def test_grouped_key_heads(dt, Hk):
+    _prefill_case(21, [150, 70], Hk, 4, 128, 128, dt, gates="plain")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_gate_preactivations(dt):
+    _prefill_case(22, [200, 129], 3, 3, 128, 128, dt, gates="pre")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("norm,z_act", [(True, None), (False, "sigmoid"), (True, "none"), (True, "sigmoid")])
+def test_output_epilogue(dt, norm, z_act):
+    _prefill_case(23, [190, 64, 1], 2, 2, 128, 128, dt, gates="plain", norm=norm, z_act=z_act)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("seg", ["2", "16"])
+def test_state_slots(dt, seg, monkeypatch):
+    monkeypatch.setenv("KDA_SEG_CHUNKS", seg)
+    # shuffled slots, a padding sequence and an empty one; several segments per sequence
+    _prefill_case(24, [300, 0, 77, 260], 2, 2, 128, 128, dt, gates="plain", slots=[5, 2, -1, 0])
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64), (64, 64)])
+def test_all_options_together(dk, dv, monkeypatch):
+    monkeypatch.setenv("KDA_SEG_CHUNKS", "2")
+    _prefill_case(25, [333, 5, 180], 2, 4, dk, dv, "bf16", gates="pre", norm=True, z_act="sigmoid",
+                  slots=[1, 3, 0])
+
+
+def test_all_options_fp32():
+    _prefill_case(26, [140, 70], 1, 2, 64, 64, "f32", gates="pre", norm=True, z_act="sigmoid", slots=[2, 0])
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_decode_options(dt):
+    bf = dt == "bf16"
+    B, Hk, H, K, V, slots_n = 8, 2, 4, 128, 128, 12
+    rng = np.random.default_rng(27)
+    state = (0.02 * rng.standard_normal((slots_n, H, K, V))).astype(np.float32)
+    si = rng.permutation(slots_n)[:B].astype(np.int32)
+    dstate = torch.from_numpy(state).cuda()
+    ref_state = state.astype(np.float64)
+    tol = gc.TOL_BF16 if bf else gc.TOL_F32
+    for step in range(3):
+        x = inputs.option_inputs(270 + step, B, Hk, H, K, V, dt)
+        ref_o = oo.decode_ex(x["q"], x["k"], x["v"], ref_state, si, gate_x=x["gate_x"], beta_y=x["beta_y"],
+                             gate_scale=0.1, norm=True, norm_eps=1e-5, norm_weight=x["norm_weight"],
+                             out_gate=x["out_gate"], out_gate_act="sigmoid")
+        o = kda.kda_decode_step_ex(_t(x["q"], bf), _t(x["k"], bf), _t(x["v"], bf), dstate,
+                                   torch.from_numpy(si).cuda(), gate_x=_t(x["gate_x"], bf),
+                                   beta_y=_t(x["beta_y"], bf), gate_scale=0.1, norm=True, norm_eps=1e-5,
+                                   norm_weight=_t(x["norm_weight"], False), out_gate=_t(x["out_gate"], bf),
+                                   out_gate_act="sigmoid")
+        torch.cuda.synchronize()
+        gc.assert_close(f"o step {step}", gc.host(o), ref_o, tol, bf16_rounded=bf)
+    gc.assert_close("state", gc.host(dstate), ref_state, tol)
+
+
+def test_extended_entry_points_without_options_match_the_plain_ones():
+    inp = inputs.prefill_inputs(28, [130, 61], 2, 128, 128, "bf16", 0.1, "random")
+    d = gc.to_device(inp)
+    o1, s1 = gc.run_prefill(d)
+    o2, s2 = kda.kda_chunk_fwd_ex(d["q"], d["k"], d["v"], d["cu_seqlens"], log_alpha=d["log_alpha"],
+                                  beta=d["beta"], initial_state=d["initial_state"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
