@@ -44,6 +44,29 @@ def prefill_flops_per_token_head(K, V, c=C):
             + c ** 3 / 3 + 6 * c * K * V) / c
 
 
+def fused_prefill_bytes(T, H, K, V, N, in_bytes=2, out_bytes=2):
+    """Algorithmic bytes of the extended call with gate pre-activations and the
+    output epilogue: q, k, v, gate_x ([T,H,K]), beta_y ([T,H]) and the output gate
+    z ([T,H,V]) read once in the input type, o written once, the d_v norm
+    weight, and the initial and final states."""
+    per_tok_head = (3 * K + V + 1 + V) * in_bytes + V * out_bytes
+    return T * H * per_tok_head + 4 * V + N * H * K * V * 4 * 2
+
+
+def time_calls(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def decode_bytes(B, H, K, V, in_bytes=2, out_bytes=2):
     return B * H * (2 * K * V * 4 + 2 * K * in_bytes + K * 4 + 4 + V * in_bytes + V * out_bytes)
 
@@ -133,6 +156,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the extended-entry-point measurements")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of this many MiB (for HBM counter scaling)")
     args = ap.parse_args()
@@ -218,6 +243,34 @@ def main():
                        "median": round(sorted(per)[len(per) // 2], 4)},
     }
 
+    # ---- the same workload through kda_chunk_fwd_ex: bf16 gate pre-activations
+    # (log alpha = -0.05 softplus(x), beta = sigmoid(y)) and the RMS-norm + sigmoid
+    # output-gate epilogue fused into the output pass
+    if not args.no_variants:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(20)
+        gx = torch.randn((T, H, K), generator=gen, device=dev).to(torch.bfloat16)
+        by = torch.randn((T, H), generator=gen, device=dev).to(torch.bfloat16)
+        z = torch.randn((T, H, V), generator=gen, device=dev).to(torch.bfloat16)
+        nw = 1 + 0.1 * torch.randn((V,), generator=gen, device=dev)
+
+        def fused():
+            kda.kda_chunk_fwd_ex(d["q"], d["k"], d["v"], d["cu_seqlens"], gate_x=gx, beta_y=by,
+                                 gate_scale=0.05, norm=True, norm_eps=1e-6, norm_weight=nw, out_gate=z,
+                                 out_gate_act="sigmoid", initial_state=d["initial_state"], final_state=sT,
+                                 o=o, stream=stream)
+
+        fms = time_calls(fused, args.steps, args.warmup, stream)
+        fb = fused_prefill_bytes(T, H, K, V, N)
+        fgbs = fb / (fms / 1e3) / 1e9
+        result["variants"] = {"fused_gates_norm_gate": {
+            "entry": "kda_chunk_fwd_ex (gate_x, beta_y bf16; norm + weight; sigmoid output gate)",
+            "workload": name, "ms_per_step": round(fms, 4), "value": round(T / (fms / 1e3) / 1e6, 3),
+            "unit": "Mtokens/s",
+            "roofline": {"bound": "hbm", "achieved": round(fgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(fgbs / PEAK_HBM_GBS, 4), "algorithmic_bytes_per_launch": fb}}}
+        del gx, by, z
+
     cpu_d = None
     if not args.no_cpu_baseline:
         cpu_d = {n: d[n] for n in ("q", "k", "v", "log_alpha", "beta", "initial_state")}
@@ -245,17 +298,75 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / steps
+        # the plain steps from a captured HIP graph as well
+        Gp = min(steps, 64)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for s in range(Gp):
+                kda.kda_decode_step(dd["q"][s], dd["k"][s], dd["v"][s], dd["log_alpha"][s], dd["beta"][s],
+                                    state, o=od)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        pgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(pgraph):
+            for s in range(Gp):
+                kda.kda_decode_step(dd["q"][s], dd["k"][s], dd["v"][s], dd["log_alpha"][s], dd["beta"][s],
+                                    state, o=od)
+        graph_us = time_calls(pgraph.replay, max(1, steps // Gp), 1, stream) * 1e3 / Gp
+        del pgraph
         dbytes = decode_bytes(Bd, Hd, Kd, Vd)
         dgbs = dbytes / (us / 1e6) / 1e9
         result["decode"] = {
             "value": round(us, 3), "unit": "us/step", "steps": steps,
             "workload": "decode_b64: B=64, H=32, d_k=d_v=128, fp32 state cache (128 MiB), "
                         "bf16 q/k/v/o, fresh inputs every step",
+            "graph_us_per_step": round(graph_us, 3),
             "roofline": {"bound": "hbm", "achieved": round(dgbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(dgbs / PEAK_HBM_GBS, 4),
                          "traffic": measured_traffic("decode_b64.md"),
                          "algorithmic_bytes_per_launch": dbytes},
         }
+        if not args.no_variants:
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(21)
+            dgx = torch.randn((min(steps, 64), Bd, Hd, Kd), generator=gen, device=dev).to(torch.bfloat16)
+            dby = torch.randn((min(steps, 64), Bd, Hd), generator=gen, device=dev).to(torch.bfloat16)
+            dz = torch.randn((min(steps, 64), Bd, Hd, Vd), generator=gen, device=dev).to(torch.bfloat16)
+            dnw = 1 + 0.1 * torch.randn((Vd,), generator=gen, device=dev)
+            it = [0]
+
+            def dfused():
+                s = it[0] % dgx.shape[0]
+                it[0] += 1
+                # on the current stream, which is the capture stream while the graph is recorded
+                kda.kda_decode_step_ex(dd["q"][s], dd["k"][s], dd["v"][s], state, gate_x=dgx[s], beta_y=dby[s],
+                                       gate_scale=0.1, norm=True, norm_weight=dnw, out_gate=dz[s],
+                                       out_gate_act="sigmoid", o=od)
+
+            dus = time_calls(dfused, steps, min(args.warmup, steps), stream) * 1e3
+            # the same steps from a captured HIP graph (no per-call host work)
+            G = dgx.shape[0]
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                it[0] = 0
+                for _ in range(G):
+                    dfused()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            it[0] = 0
+            with torch.cuda.graph(graph):
+                for _ in range(G):
+                    dfused()
+            reps = max(1, steps // G)
+            gus = time_calls(graph.replay, reps, 1, stream) * 1e3 / G
+            result["decode"]["variants"] = {"fused_gates_norm_gate": {
+                "entry": "kda_decode_step_ex (gate_x, beta_y bf16; norm + weight; sigmoid output gate)",
+                "value": round(gus, 3), "unit": "us/step", "timing": f"HIP graph of {G} steps, {reps} replays",
+                "eager_us_per_step": round(dus, 3)}}
+            del graph
         if cpu_d is not None:
             result["decode"]["cpu_baseline"] = cpu_baseline_decode(dd)
         del dd, state

@@ -137,3 +137,52 @@ def test_extended_entry_points_without_options_match_the_plain_ones():
                                   beta=d["beta"], initial_state=d["initial_state"])
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_decode_steps_replayed_from_a_hip_graph_match_eager():
+    """Decode steps (plain and extended) captured once in a HIP graph and replayed
+    three times, with eager work and synchronisation between the replays, give
+    bitwise the eager outputs and states."""
+    B, H, K, V, steps = 8, 4, 128, 128, 3
+    rng = np.random.default_rng(29)
+    state0 = torch.from_numpy((0.02 * rng.standard_normal((B, H, K, V))).astype(np.float32)).cuda()
+    xs = [inputs.option_inputs(290 + s, B, 2, H, K, V, "bf16") for s in range(steps)]
+    dev = [{n: _t(x[n], n != "norm_weight") for n in x} for x in xs]
+    la = [torch.from_numpy((-0.1 * oo.softplus(x["gate_x"])).astype(np.float32)).cuda() for x in xs]
+    be = [torch.from_numpy(oo.sigmoid(x["beta_y"]).astype(np.float32)).cuda() for x in xs]
+    outs = [torch.empty((B, H, V), dtype=torch.bfloat16, device="cuda") for _ in range(2 * steps)]
+    state = state0.clone()
+
+    def run():
+        for s in range(steps):
+            d = dev[s]
+            kda.kda_decode_step_ex(d["q"], d["k"], d["v"], state, log_alpha=la[s], beta=be[s], o=outs[2 * s])
+            kda.kda_decode_step_ex(d["q"], d["k"], d["v"], state, gate_x=d["gate_x"], beta_y=d["beta_y"],
+                                   gate_scale=0.1, norm=True, norm_weight=d["norm_weight"], out_gate=d["out_gate"],
+                                   out_gate_act="sigmoid", o=outs[2 * s + 1])
+
+    run()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    ref_state = state.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm the capture stream first, as torch graph capture expects
+        state.copy_(state0)
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    state.copy_(state0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(3):
+        state.copy_(state0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, r in zip(outs, ref):
+            assert torch.equal(o, r), f"replay {rep}: output differs from eager"
+        assert torch.equal(state, ref_state), f"replay {rep}: state differs from eager"
+        _ = (state * 2).sum().item()   # eager work between replays
