@@ -198,13 +198,32 @@ __device__ __forceinline__ PrepItem prep_item(const PrefillArgs &a, const int32_
 
 // The inputs one lane reads for a work item: token 16w + r of the chunk, channels
 // 32 cb + 16 hf + 4g .. + 3 (bf16 q and k as raw pairs, log decay fp32), and beta.
-// With GX the log decay comes from bf16 gate pre-activations (log alpha =
-// -gscale softplus(x)) instead of fp32 log alpha.
+// The inputs one lane reads for a work item: token 16w + r of the chunk and, per
+// 32-channel block, the 8 consecutive channels o(g) .. o(g) + 7 with
+// o(g) = 16 (g & 1) + 8 (g >> 1), so every k, q (and bf16 gate) load is 16 bytes.
+// One v_permlane16_swap per register pair (it exchanges the odd 16-lane rows of
+// its first operand with the even rows of its second) then leaves lane g with
+// channels 4g .. 4g + 3 in the first result and 16 + 4g .. 16 + 4g + 3 in the
+// second: the chain order k(g, e) of the MFMA operands. With GX the log decay
+// comes from bf16 gate pre-activations (log alpha = -gscale softplus(x)) instead
+// of fp32 log alpha.
+__device__ __forceinline__ void swap16(uint32_t &a, uint32_t &b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
+}
+__device__ __forceinline__ void swap16(float &a, float &b) {
+    uint32_t x = __float_as_uint(a), y = __float_as_uint(b);
+    swap16(x, y);
+    a = __uint_as_float(x);
+    b = __uint_as_float(y);
+}
+
 template <int K, bool GX>
 struct PrepRaw {
-    using GT = typename std::conditional<GX, uint2, float4>::type;
-    GT gv[K / 32][2];
-    uint2 kv[K / 32][2], qv[K / 32][2];
+    float4 gv[K / 32][2];  // fp32 log alpha: channels o(g) .. + 3 and o(g) + 4 .. + 7 (without GX)
+    uint4 xv[K / 32];      // bf16 gate pre-activation, 8 channels (with GX)
+    uint4 kv[K / 32], qv[K / 32];
     float beta;
     bool valid;  // token inside the sequence (else its k, q, decay and beta count as zero)
 
@@ -215,48 +234,69 @@ struct PrepRaw {
         const size_t t = static_cast<size_t>(it.t0 + (valid ? tr : 0));
         const size_t tok = t * a.H + it.h;
         const size_t row = tok * K, rowk = (t * a.Hk + it.h / (a.H / a.Hk)) * K;
+        const int o = 16 * (g & 1) + 8 * (g >> 1);
 #pragma unroll
-        for (int cb = 0; cb < K / 32; ++cb)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const int ch = 32 * cb + 16 * hf + 4 * g;
-                if constexpr (GX)
-                    gv[cb][hf] = *reinterpret_cast<const uint2 *>(static_cast<const bf16_t *>(a.gx) + row + ch);
-                else
-                    gv[cb][hf] = *reinterpret_cast<const float4 *>(a.g + row + ch);
-                kv[cb][hf] = *reinterpret_cast<const uint2 *>(static_cast<const bf16_t *>(a.k) + rowk + ch);
-                qv[cb][hf] = *reinterpret_cast<const uint2 *>(static_cast<const bf16_t *>(a.q) + rowk + ch);
+        for (int cb = 0; cb < K / 32; ++cb) {
+            const int ch = 32 * cb + o;
+            if constexpr (GX) {
+                xv[cb] = *reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.gx) + row + ch);
+            } else {
+                gv[cb][0] = *reinterpret_cast<const float4 *>(a.g + row + ch);
+                gv[cb][1] = *reinterpret_cast<const float4 *>(a.g + row + ch + 4);
             }
+            kv[cb] = *reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.k) + rowk + ch);
+            qv[cb] = *reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.q) + rowk + ch);
+        }
         beta = a.by ? bf16_to_f32(static_cast<const bf16_t *>(a.by)[tok]) : a.beta[tok];
     }
     // k, q and the inclusive scan of the log decay over the 16-token sub-chunk
-    // (lanes r of a 16-lane row are its consecutive tokens)
+    // (lanes r of a 16-lane row are its consecutive tokens), channels in chain order
     __device__ __forceinline__ void unpack(float (&kx)[K / 32][8], float (&qx)[K / 32][8], float (&sc)[K / 32][8],
                                            float gscale) const {
 #pragma unroll
-        for (int cb = 0; cb < K / 32; ++cb)
+        for (int cb = 0; cb < K / 32; ++cb) {
+            uint4 kk = kv[cb], qq = qv[cb];
+            swap16(kk.x, kk.z);
+            swap16(kk.y, kk.w);
+            swap16(qq.x, qq.z);
+            swap16(qq.y, qq.w);
+            float gg[8];
+            if constexpr (GX) {
+                uint4 xx = xv[cb];
+                swap16(xx.x, xx.z);
+                swap16(xx.y, xx.w);
+                const uint32_t w4[4] = {xx.x, xx.y, xx.z, xx.w};
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                float4 gg;
-                if constexpr (GX) {
-                    const uint2 xx = gv[cb][hf];
-                    gg = make_float4(log_alpha_from(__uint_as_float(xx.x << 16), gscale),
-                                     log_alpha_from(__uint_as_float(xx.x & 0xFFFF0000u), gscale),
-                                     log_alpha_from(__uint_as_float(xx.y << 16), gscale),
-                                     log_alpha_from(__uint_as_float(xx.y & 0xFFFF0000u), gscale));
-                } else {
-                    gg = gv[cb][hf];
+                for (int e = 0; e < 4; ++e) {
+                    gg[2 * e] = log_alpha_from(__uint_as_float(w4[e] << 16), gscale);
+                    gg[2 * e + 1] = log_alpha_from(__uint_as_float(w4[e] & 0xFFFF0000u), gscale);
                 }
-                if (!valid) gg = make_float4(0.f, 0.f, 0.f, 0.f);
-                const uint2 kk = valid ? kv[cb][hf] : make_uint2(0u, 0u);
-                const uint2 qq = valid ? qv[cb][hf] : make_uint2(0u, 0u);
-                sc[cb][4 * hf + 0] = gg.x; sc[cb][4 * hf + 1] = gg.y;
-                sc[cb][4 * hf + 2] = gg.z; sc[cb][4 * hf + 3] = gg.w;
-                kx[cb][4 * hf + 0] = __uint_as_float(kk.x << 16); kx[cb][4 * hf + 1] = __uint_as_float(kk.x & 0xFFFF0000u);
-                kx[cb][4 * hf + 2] = __uint_as_float(kk.y << 16); kx[cb][4 * hf + 3] = __uint_as_float(kk.y & 0xFFFF0000u);
-                qx[cb][4 * hf + 0] = __uint_as_float(qq.x << 16); qx[cb][4 * hf + 1] = __uint_as_float(qq.x & 0xFFFF0000u);
-                qx[cb][4 * hf + 2] = __uint_as_float(qq.y << 16); qx[cb][4 * hf + 3] = __uint_as_float(qq.y & 0xFFFF0000u);
+            } else {
+                float4 p = gv[cb][0], q4 = gv[cb][1];
+                swap16(p.x, q4.x);
+                swap16(p.y, q4.y);
+                swap16(p.z, q4.z);
+                swap16(p.w, q4.w);
+                gg[0] = p.x; gg[1] = p.y; gg[2] = p.z; gg[3] = p.w;
+                gg[4] = q4.x; gg[5] = q4.y; gg[6] = q4.z; gg[7] = q4.w;
             }
+            const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w}, qw[4] = {qq.x, qq.y, qq.z, qq.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kx[cb][2 * e] = __uint_as_float(kw[e] << 16);
+                kx[cb][2 * e + 1] = __uint_as_float(kw[e] & 0xFFFF0000u);
+                qx[cb][2 * e] = __uint_as_float(qw[e] << 16);
+                qx[cb][2 * e + 1] = __uint_as_float(qw[e] & 0xFFFF0000u);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                sc[cb][e] = valid ? gg[e] : 0.f;
+                if (!valid) {
+                    kx[cb][e] = 0.f;
+                    qx[cb][e] = 0.f;
+                }
+            }
+        }
 #pragma unroll
         for (int cb = 0; cb < K / 32; ++cb)
 #pragma unroll
@@ -1109,7 +1149,7 @@ __global__ __launch_bounds__(64 * (K + V) / 32) void seg_kernel(PrefillArgs a, c
 // 16 state columns per workgroup, fp32
 template <int K, int V>
 __global__ __launch_bounds__(256) void prefix_kernel(const int32_t *soff, int N, int H, SegBufs sb) {
-    __shared__ float m[K][K + 4];
+    __shared__ __attribute__((aligned(16))) float m[K][K + 4];
     __shared__ float x[K][16];
     constexpr int NV = V / 16, RPT = K / 16;
     const int b = blockIdx.x, vt = b % NV, nh = b / NV, n = nh / H, h = nh - (nh / H) * H;
@@ -1127,24 +1167,20 @@ __global__ __launch_bounds__(256) void prefix_kernel(const int32_t *soff, int N,
         const float *mg = sb.mapm + (static_cast<size_t>(s0 + gl) * H + h) * K * K;
         const float *ng = sb.mapn + (static_cast<size_t>(s0 + gl) * H + h) * kv;
         for (int p = tid; p < K * K / 4; p += 256) {
-            const float4 v = reinterpret_cast<const float4 *>(mg)[p];
             const int row = (4 * p) / K, c4 = (4 * p) % K;
-            m[row][c4 + 0] = v.x; m[row][c4 + 1] = v.y; m[row][c4 + 2] = v.z; m[row][c4 + 3] = v.w;
+            *reinterpret_cast<float4 *>(&m[row][c4]) = reinterpret_cast<const float4 *>(mg)[p];
         }
         __syncthreads();
         float y[RPT];
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int row = rg * RPT + i;
-            float acc = ng[static_cast<size_t>(row) * V + vt * 16 + col];
-            for (int kk = 0; kk < K; kk += 4) {
-                const float4 mv = *reinterpret_cast<const float4 *>(&m[row][kk]);
-                acc = fmaf(mv.x, x[kk][col], acc);
-                acc = fmaf(mv.y, x[kk + 1][col], acc);
-                acc = fmaf(mv.z, x[kk + 2][col], acc);
-                acc = fmaf(mv.w, x[kk + 3][col], acc);
+        for (int i = 0; i < RPT; ++i) y[i] = ng[static_cast<size_t>(rg * RPT + i) * V + vt * 16 + col];
+        for (int kk = 0; kk < K; kk += 4) {
+            const float x0 = x[kk][col], x1 = x[kk + 1][col], x2 = x[kk + 2][col], x3 = x[kk + 3][col];
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const float4 mv = *reinterpret_cast<const float4 *>(&m[rg * RPT + i][kk]);
+                y[i] = fmaf(mv.x, x0, fmaf(mv.y, x1, fmaf(mv.z, x2, fmaf(mv.w, x3, y[i]))));
             }
-            y[i] = acc;
         }
         __syncthreads();
 #pragma unroll
