@@ -13,9 +13,13 @@
 // Mapping: one 256-thread workgroup per (b, h). A state row of d_v floats is
 // covered by d_v/4 lanes reading float4, so one wave load instruction reads
 // 64 * 16 B = 1 KiB of consecutive rows (fully coalesced). Each lane keeps its
-// d_k*d_v/1024 float4s in registers between the read and the write. The two
-// column reductions over d_k run in registers, across lanes of a wave with
-// xor-shuffles, and across the four waves through 2 KiB of LDS.
+// d_k*d_v/1024 float4s in registers between the read and the write. The small
+// inputs are loaded first, so that they arrive while the state loads are in
+// flight: one load per key channel of the gate, k and q (staged through LDS as
+// (alpha, k, q) for the lanes of every row), and each lane's four columns of v,
+// and of the norm weight and output gate when given. The two column reductions
+// over d_k run in registers, across lanes of a wave with xor-shuffles, and
+// across the four waves through LDS.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -30,40 +34,62 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
     constexpr int RPI = 64 / LPR;                    // rows per wave load
     constexpr int ITERS = K / (kDecWaves * RPI);     // float4 per lane
     static_assert(ITERS * kDecWaves * RPI == K, "row mapping must cover d_k");
+    static_assert(K % 64 == 0 && K <= 64 * kDecWaves, "one key channel per thread of the first waves");
+    __shared__ float4 vec[K];  // (alpha, k, q, -) per key channel
+    __shared__ float kqp[K / 64];
     __shared__ float4 red_r[kDecWaves][LPR];
     __shared__ float4 red_p[kDecWaves][LPR];
 
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int c4 = lane % LPR, rsub = lane / LPR;
     const int bh = blockIdx.x;
     const int b = bh / a.H, h = bh - b * a.H;
-    const int slot = a.slot_idx ? a.slot_idx[b] : b;
-    float *S = a.state + (static_cast<size_t>(slot) * a.H + h) * static_cast<size_t>(K * V);
     // value head h reads key head h / (H / Hk)
     const size_t bhk = static_cast<size_t>(b) * a.Hk + h / (a.H / a.Hk);
-    const TIn *qp = static_cast<const TIn *>(a.q) + bhk * K;
-    const TIn *kp = static_cast<const TIn *>(a.k) + bhk * K;
-    const TIn *vp = static_cast<const TIn *>(a.v) + static_cast<size_t>(bh) * V;
-    const float *gp = a.g + static_cast<size_t>(bh) * K;
-    const TIn *gxp = static_cast<const TIn *>(a.gx) + static_cast<size_t>(bh) * K;
 
+    // ---- small inputs first
+    float gk = 0.f, kk = 0.f, qk = 0.f;
+    if (tid < K) {
+        gk = a.gx ? io<TIn>::load(static_cast<const TIn *>(a.gx) + static_cast<size_t>(bh) * K + tid)
+                  : a.g[static_cast<size_t>(bh) * K + tid];
+        kk = io<TIn>::load(static_cast<const TIn *>(a.k) + bhk * K + tid);
+        qk = io<TIn>::load(static_cast<const TIn *>(a.q) + bhk * K + tid);
+    }
+    const float4 vv = io<TIn>::load4(static_cast<const TIn *>(a.v) + static_cast<size_t>(bh) * V + c4 * 4);
+    const float braw = a.by ? io<TIn>::load(static_cast<const TIn *>(a.by) + bh) : a.beta[bh];
+    float4 zv = make_float4(1.f, 1.f, 1.f, 1.f), wv = zv;
+    if (a.z) zv = io<TIn>::load4(static_cast<const TIn *>(a.z) + static_cast<size_t>(bh) * V + c4 * 4);
+    if (a.norm && a.nw) wv = io<float>::load4(a.nw + c4 * 4);
+
+    // ---- the state
+    const int slot = a.slot_idx ? ld_meta(a.slot_idx, b) : b;
+    float *S = a.state + (static_cast<size_t>(slot) * a.H + h) * static_cast<size_t>(K * V);
     float4 s[ITERS];
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
         const int row = (it * kDecWaves + w) * RPI + rsub;
         s[it] = io<float>::load4(S + row * V + c4 * 4);
     }
-    float kr[ITERS];
+
+    if (tid < K) {
+        const float al = __expf(a.gx ? log_alpha_from(gk, a.gscale) : gk);
+        vec[tid] = make_float4(al, kk, qk, 0.f);
+        float kq = kk * qk;
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) kq += __shfl_xor(kq, m);
+        if (lane == 0) kqp[w] = kq;
+    }
+    __syncthreads();
+
+    // S' = Diag(alpha) S; r = S'^T k; p = S'^T q
     float4 r4 = make_float4(0.f, 0.f, 0.f, 0.f), p4 = r4;
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
         const int row = (it * kDecWaves + w) * RPI + rsub;
-        const float al = __expf(a.gx ? log_alpha_from(io<TIn>::load(gxp + row), a.gscale) : gp[row]);
-        const float kv = io<TIn>::load(kp + row), qv = io<TIn>::load(qp + row);
-        s[it] = s[it] * al;
-        r4 = fma4(s[it], kv, r4);
-        p4 = fma4(s[it], qv, p4);
-        kr[it] = kv;
+        const float4 c = vec[row];
+        s[it] = s[it] * c.x;
+        r4 = fma4(s[it], c.y, r4);
+        p4 = fma4(s[it], c.z, p4);
     }
 #pragma unroll
     for (int m = LPR; m < 64; m <<= 1) {
@@ -76,10 +102,6 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
         red_r[w][c4] = r4;
         red_p[w][c4] = p4;
     }
-    float kq = 0.f;
-    for (int i = lane; i < K; i += 64) kq += io<TIn>::load(kp + i) * io<TIn>::load(qp + i);
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) kq += __shfl_xor(kq, m);
     __syncthreads();
     float4 r = red_r[0][c4], p = red_p[0][c4];
 #pragma unroll
@@ -87,21 +109,20 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
         r = r + red_r[ww][c4];
         p = p + red_p[ww][c4];
     }
-    const float bt = a.by ? sigmoid_f(io<TIn>::load(static_cast<const TIn *>(a.by) + bh)) : a.beta[bh];
-    const float4 u = (io<TIn>::load4(vp + c4 * 4) - r) * bt;
+    float kq = kqp[0];
+#pragma unroll
+    for (int i = 1; i < K / 64; ++i) kq += kqp[i];
+    const float bt = a.by ? sigmoid_f(braw) : braw;
+    const float4 u = (vv - r) * bt;
     float4 ov = fma4(u, kq, p) * a.scale;
     if (a.norm) {  // o / sqrt(mean o^2 + eps) over the LPR lanes of the row (uniform branch)
         float ss = ov.x * ov.x + ov.y * ov.y + ov.z * ov.z + ov.w * ov.w;
 #pragma unroll
         for (int m = 1; m < LPR; m <<= 1) ss += __shfl_xor(ss, m);
         ov = ov * rsqrtf(ss / V + a.eps);
-        if (a.nw) {
-            const float4 wv = io<float>::load4(a.nw + c4 * 4);
-            ov = make_float4(ov.x * wv.x, ov.y * wv.y, ov.z * wv.z, ov.w * wv.w);
-        }
+        ov = make_float4(ov.x * wv.x, ov.y * wv.y, ov.z * wv.z, ov.w * wv.w);
     }
     if (a.z) {
-        const float4 zv = io<TIn>::load4(static_cast<const TIn *>(a.z) + static_cast<size_t>(bh) * V + c4 * 4);
         ov = make_float4(ov.x * out_gate_act(zv.x, a.zact), ov.y * out_gate_act(zv.y, a.zact),
                          ov.z * out_gate_act(zv.z, a.zact), ov.w * out_gate_act(zv.w, a.zact));
     }
@@ -109,10 +130,11 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
         TOut *op = static_cast<TOut *>(a.o) + static_cast<size_t>(bh) * V;
         io<TOut>::store4(op + c4 * 4, ov);
     }
+    // S = S' + k u^T
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
         const int row = (it * kDecWaves + w) * RPI + rsub;
-        io<float>::store4(S + row * V + c4 * 4, fma4(u, kr[it], s[it]));
+        io<float>::store4(S + row * V + c4 * 4, fma4(u, vec[row].y, s[it]));
     }
 }
 

@@ -51,6 +51,14 @@ template <> struct io<bf16_t> {
     }
 };
 
+// Read-only int32 metadata (offsets, sequence bounds, slot indices) that no
+// kernel of the launch writes: read through the constant address space, so that
+// a uniform index becomes a scalar load. A vector load would be counted with the
+// stores in flight, and its first use would wait for all of them.
+__device__ __forceinline__ int32_t ld_meta(const int32_t *p, int i) {
+    return ((const __attribute__((address_space(4))) int32_t *)p)[i];
+}
+
 // Gate activations of the extended entry points (kda_options_t):
 // log alpha = -scale * softplus(x), softplus(x) = ln(1 + e^x) = max(x, 0) + ln(1 + e^-|x|);
 // beta = sigmoid(y) = 1 / (1 + e^-y).

@@ -52,6 +52,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
+
 constexpr int kC = 64;
 constexpr float kFastRange = 10.f;  // max decay exponent of one sub-chunk on the fp16 path
 
@@ -190,10 +191,10 @@ __device__ __forceinline__ PrepItem prep_item(const PrefillArgs &a, const int32_
     int lo = 0, hi = a.N - 1;  // sequence n with off[n] <= c < off[n + 1]
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= c) lo = mid; else hi = mid - 1;
+        if (ld_meta(off, mid) <= c) lo = mid; else hi = mid - 1;
     }
-    const int t0 = a.cu_seqlens[lo] + (c - off[lo]) * kC;
-    return PrepItem{c, h, lo, t0, min(kC, a.cu_seqlens[lo + 1] - t0)};
+    const int t0 = ld_meta(a.cu_seqlens, lo) + (c - ld_meta(off, lo)) * kC;
+    return PrepItem{c, h, lo, t0, min(kC, ld_meta(a.cu_seqlens, lo + 1) - t0)};
 }
 
 // The inputs one lane reads for a work item: token 16w + r of the chunk, channels
@@ -224,7 +225,7 @@ struct PrepRaw {
     float4 gv[K / 32][2];  // fp32 log alpha: channels o(g) .. + 3 and o(g) + 4 .. + 7 (without GX)
     uint4 xv[K / 32];      // bf16 gate pre-activation, 8 channels (with GX)
     uint4 kv[K / 32], qv[K / 32];
-    float beta;
+    uint32_t betaw;  // beta as loaded: fp32 bits, or bf16 bits of its pre-activation
     bool valid;  // token inside the sequence (else its k, q, decay and beta count as zero)
 
     // Loads are unconditional: a token past the sequence end reads token t0 of the chunk.
@@ -247,7 +248,14 @@ struct PrepRaw {
             kv[cb] = *reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.k) + rowk + ch);
             qv[cb] = *reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.q) + rowk + ch);
         }
-        beta = a.by ? bf16_to_f32(static_cast<const bf16_t *>(a.by)[tok]) : a.beta[tok];
+        // raw bits: converting here would make the wave wait for the load at once
+        if (a.by) betaw = static_cast<const bf16_t *>(a.by)[tok];
+        else betaw = reinterpret_cast<const uint32_t *>(a.beta)[tok];
+    }
+    // beta (sigmoid of the bf16 pre-activation when given), 0 past the sequence end
+    __device__ __forceinline__ float beta(const PrefillArgs &a) const {
+        if (!valid) return 0.f;
+        return a.by ? sigmoid_f(__uint_as_float(betaw << 16)) : __uint_as_float(betaw);
     }
     // k, q and the inclusive scan of the log decay over the 16-token sub-chunk
     // (lanes r of a 16-lane row are its consecutive tokens), channels in chain order
@@ -320,7 +328,7 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
     constexpr int NCB = K / 32, NCT = K / 16;
     using R = Rec<K>;
     __shared__ PrepSmem<K> sm;
-    const int total = off[a.N] * a.H;
+    const int total = ld_meta(off, a.N) * a.H;
     const int tid = threadIdx.x, l = tid & 63, r = l & 15, g = l >> 4;
     // wave index as a scalar: branches on it must be real jumps, because a
     // matrix instruction inside an EXEC-masked block still writes its result
@@ -337,7 +345,7 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
 
     float kx[NCB][8], qx[NCB][8], s[NCB][8];
     raw.unpack(kx, qx, s, a.gscale);
-    if (g == 0) sm.beta[tr] = raw.valid ? (a.by ? sigmoid_f(raw.beta) : raw.beta) : 0.f;
+    if (g == 0) sm.beta[tr] = raw.beta(a);
     if (r == 15) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
