@@ -162,7 +162,10 @@ __global__ __launch_bounds__(256) void chunk_offsets_kernel(const int32_t *cu, i
 // prep: state-independent work of one chunk of one head
 template <int K>
 struct PrepSmem {
-    static constexpr int NCB = K / 32, LD = 65;
+    // row stride of the fp32 64 x 64 matrices: with 68 (= 4 mod 64) words, the
+    // accumulator layout (rows 4g + e, column r) and the A-operand reads (row r,
+    // columns 4s + g) both spread a wave's 64 lanes over distinct banks
+    static constexpr int NCB = K / 32, LD = 68;
     float tot[4][K];       // decay of each sub-chunk per channel (log, <= 0)
     float fac[16][K + 4];  // per-channel factors, see prep_kernel
     float beta[kC];
