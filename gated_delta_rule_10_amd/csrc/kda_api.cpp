@@ -39,15 +39,17 @@ bool force_valu() {
 namespace {
 
 // Options: neutral values when `opt` is NULL; otherwise checked against the
-// sizes. Returns KDA_OK or the status to report.
+// sizes. `tokens`: the call has tokens (without any, no gate is read and both
+// gate forms may be absent). Returns KDA_OK or the status to report.
 kda_status_t check_options(const kda_options_t *opt, int32_t H, bool has_log_alpha, bool has_beta,
-                           bool prefill, kda_options_t &o) {
+                           bool prefill, bool tokens, kda_options_t &o) {
     o = kda_options_t{};
     if (opt) o = *opt;
     if (o.num_k_heads == 0) o.num_k_heads = H;
     if (o.num_k_heads < 1 || H % o.num_k_heads != 0) return KDA_ERR_INVALID_ARG;
-    if ((o.gate_x != nullptr) == has_log_alpha) return KDA_ERR_INVALID_ARG;  // exactly one gate form
-    if ((o.beta_y != nullptr) == has_beta) return KDA_ERR_INVALID_ARG;
+    // one gate form of each kind, never both
+    if ((o.gate_x && has_log_alpha) || (o.beta_y && has_beta)) return KDA_ERR_INVALID_ARG;
+    if (tokens && ((!o.gate_x && !has_log_alpha) || (!o.beta_y && !has_beta))) return KDA_ERR_INVALID_ARG;
     if (o.gate_x && !(o.gate_scale > 0.f && o.gate_scale < 3.0e38f)) return KDA_ERR_INVALID_ARG;
     if (!(o.norm_eps >= 0.f && o.norm_eps < 3.0e38f)) return KDA_ERR_INVALID_ARG;
     if (o.out_gate_act != KDA_ACT_NONE && o.out_gate_act != KDA_ACT_SIGMOID) return KDA_ERR_INVALID_ARG;
@@ -71,7 +73,7 @@ kda_status_t chunk_fwd(const void *q, const void *k, const void *v, const float 
     if (!dtype_valid(in_dtype) || !dtype_valid(out_dtype)) return KDA_ERR_INVALID_ARG;
     if (!cu_seqlens || !aligned16(cu_seqlens)) return KDA_ERR_INVALID_ARG;
     kda_options_t op;
-    const kda_status_t os = check_options(opt, H, log_alpha != nullptr, beta != nullptr, true, op);
+    const kda_status_t os = check_options(opt, H, log_alpha != nullptr, beta != nullptr, true, T_total > 0, op);
     if (os != KDA_OK) return os;
     if (T_total > 0) {
         const void *req[] = {q, k, v, op.gate_x ? op.gate_x : log_alpha, op.beta_y ? op.beta_y : beta, o};
@@ -117,7 +119,7 @@ kda_status_t decode_step(const void *q, const void *k, const void *v, const floa
     if (B < 1 || H < 1 || num_slots < 1) return KDA_ERR_INVALID_ARG;
     if (!dtype_valid(in_dtype) || !dtype_valid(out_dtype)) return KDA_ERR_INVALID_ARG;
     kda_options_t op;
-    const kda_status_t os = check_options(opt, H, log_alpha != nullptr, beta != nullptr, false, op);
+    const kda_status_t os = check_options(opt, H, log_alpha != nullptr, beta != nullptr, false, true, op);
     if (os != KDA_OK) return os;
     const void *req[] = {q, k, v, op.gate_x ? op.gate_x : log_alpha, op.beta_y ? op.beta_y : beta, state_cache, o};
     for (const void *p : req)

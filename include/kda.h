@@ -104,7 +104,8 @@ size_t kda_chunk_fwd_workspace_size(int32_t N, int32_t T_total, int32_t H,
  *   workspace   device scratch of workspace_bytes (may be NULL if the size
  *               query returns 0)
  *
- * Sizes: N >= 1, H >= 1, T_total >= 0, d_k and d_v in {64, 128}.
+ * Sizes: N >= 1, H >= 1, T_total >= 0, d_k and d_v in {64, 128}. With
+ * T_total = 0 the token arrays (q, k, v, log_alpha, beta, o) may be NULL.
  * dtype pairs: (F32 in, F32 out), (BF16 in, BF16 out), (BF16 in, F32 out).
  * Internal arithmetic: fp32 state and accumulation; the state is fp32 at
  * every chunk boundary.
@@ -206,6 +207,9 @@ typedef struct {
  * epilogue runs as a second pass over o). Errors as for kda_chunk_fwd, plus
  * KDA_ERR_INVALID_ARG for inconsistent options; kda_chunk_fwd itself returns
  * KDA_ERR_INVALID_ARG when log_alpha or beta is NULL and T_total > 0.
+ * With T_total = 0 no gate is read: neither gate form need be given (and
+ * gate_x, beta_y and out_gate may be NULL), but giving both forms of one gate
+ * is still an error.
  */
 kda_status_t kda_chunk_fwd_ex(const void *q, const void *k, const void *v,
                               const float *log_alpha, const float *beta,

@@ -79,11 +79,13 @@ def half_ulp_bf16(x: np.ndarray) -> np.ndarray:
 def err_over_rms(got, ref, bf16_rounded: bool = False) -> float:
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
+    if ref.size == 0:
+        return 0.0
     rms = float(np.sqrt(np.mean(ref * ref)))
     d = np.abs(got - ref)
     if bf16_rounded:
         d = np.maximum(d - half_ulp_bf16(np.maximum(np.abs(ref), np.abs(got))), 0.0)
-    return float(d.max()) / max(rms, 1e-30) if d.size else 0.0
+    return float(d.max()) / max(rms, 1e-30)
 
 
 def assert_close(name, got, ref, tol, bf16_rounded=False):

@@ -144,6 +144,19 @@ def test_chunk_fwd_ex_rejects_inconsistent_options(lib, opt_over, call_over):
     assert _prefill_ex(lib, opt, **call_over) == kda.KDA_ERR_INVALID_ARG
 
 
+def test_no_tokens_needs_no_gates(lib):
+    """With T_total = 0 no gate is read: missing gates pass validation (the call
+    then fails on the unsupported head size, which is checked later, before any
+    HIP call), while both forms of one gate are still rejected."""
+    none = dict(T=0, q=None, k=None, v=None, o=None, g=None, b=None, dk=96)
+    assert _prefill(lib, **none) == kda.KDA_ERR_UNSUPPORTED
+    assert _prefill_ex(lib, kda.KdaOptions(), **none) == kda.KDA_ERR_UNSUPPORTED
+    both = kda.KdaOptions()
+    both.gate_x = A
+    assert _prefill_ex(lib, both, T=0, g=A, dk=96) == kda.KDA_ERR_INVALID_ARG
+    assert _prefill(lib, T=1, g=None, dk=96) == kda.KDA_ERR_INVALID_ARG
+
+
 def test_plain_entry_point_needs_both_gates(lib):
     assert _prefill(lib, g=None) == kda.KDA_ERR_INVALID_ARG
     assert _decode(lib, b=None) == kda.KDA_ERR_INVALID_ARG

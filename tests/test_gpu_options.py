@@ -93,6 +93,13 @@ def test_state_slots(dt, seg, monkeypatch):
     _prefill_case(24, [300, 0, 77, 260], 2, 2, 128, 128, dt, gates="plain", slots=[5, 2, -1, 0])
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_no_tokens_with_slots_and_epilogue(dt):
+    # T = 0: the cache passes through (slot 2 and 0 keep their states, the padding
+    # sequence writes nothing) and there are no output rows to normalise or gate
+    _prefill_case(26, [0, 0, 0], 2, 4, 128, 128, dt, gates="pre", norm=True, z_act="sigmoid", slots=[2, -1, 0])
+
+
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64), (64, 64)])
 def test_all_options_together(dk, dv, monkeypatch):
     monkeypatch.setenv("KDA_SEG_CHUNKS", "2")

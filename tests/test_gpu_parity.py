@@ -58,6 +58,20 @@ def test_prefill_varlen_with_empty_and_single():
     assert torch.equal(sT[0], s0[0]) and torch.equal(sT[3], s0[3])
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_prefill_no_tokens_at_all(dt):
+    """Every sequence empty (T = 0): no output rows; each final state is its
+    initial state, bit for bit, and a missing initial state gives zeros."""
+    inp = inputs.prefill_inputs(10, [0, 0, 0], 4, 128, 128, dt, 0.1, "random")
+    d = gc.to_device(inp)
+    o, sT = gc.run_prefill(d)
+    assert tuple(o.shape) == (0, 4, 128)
+    assert torch.equal(sT, d["initial_state"])
+    d["initial_state"] = None
+    _, sT = gc.run_prefill(d)
+    assert torch.count_nonzero(sT).item() == 0
+
+
 def test_prefill_strong_decay():
     """Large gate magnitudes (alpha down to ~e^-6 per token)."""
     _prefill_case(inputs.prefill_inputs(9, [300], 2, 128, 128, "bf16", 3.0, "random"))
