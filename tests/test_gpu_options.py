@@ -193,3 +193,54 @@ def test_decode_steps_replayed_from_a_hip_graph_match_eager():
             assert torch.equal(o, r), f"replay {rep}: output differs from eager"
         assert torch.equal(state, ref_state), f"replay {rep}: state differs from eager"
         _ = (state * 2).sum().item()   # eager work between replays
+
+
+def test_prefill_replayed_from_a_hip_graph_matches_eager(monkeypatch):
+    """Prefill (plain and extended, several segments per sequence, so every kernel
+    of the call runs) captured once in a HIP graph with caller-provided outputs and
+    workspace, replayed three times with eager work and synchronisation between
+    the replays: outputs and final states equal the eager ones bitwise."""
+    monkeypatch.setenv("KDA_SEG_CHUNKS", "2")
+    lens = [300, 77, 500]
+    Hk, H, K, V = 2, 4, 128, 128
+    T, N = sum(lens), len(lens)
+    x = inputs.option_inputs(31, T, Hk, H, K, V, "bf16")
+    d = {n: _t(x[n], n != "norm_weight") for n in x}
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).cuda()
+    rng = np.random.default_rng(31)
+    s0 = torch.from_numpy((0.02 * rng.standard_normal((N, H, K, V))).astype(np.float32)).cuda()
+    la = torch.from_numpy((-0.1 * oo.softplus(x["gate_x"])).astype(np.float32)).cuda()
+    be = torch.from_numpy(oo.sigmoid(x["beta_y"]).astype(np.float32)).cuda()
+    o = [torch.empty((T, H, V), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    fin = [torch.empty((N, H, K, V), dtype=torch.float32, device="cuda") for _ in range(2)]
+    ws = torch.empty(kda.kda_chunk_fwd_workspace_size(N, T, H, K, V, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+
+    def run():
+        kda.kda_chunk_fwd_ex(d["q"], d["k"], d["v"], cu, log_alpha=la, beta=be, initial_state=s0,
+                             final_state=fin[0], o=o[0], workspace=ws)
+        kda.kda_chunk_fwd_ex(d["q"], d["k"], d["v"], cu, gate_x=d["gate_x"], beta_y=d["beta_y"], gate_scale=0.1,
+                             norm=True, norm_weight=d["norm_weight"], out_gate=d["out_gate"],
+                             out_gate_act="sigmoid", initial_state=s0, final_state=fin[1], o=o[1], workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in o + fin]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm the capture stream first, as torch graph capture expects
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(3):
+        for t in o + fin:
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for t, r in zip(o + fin, ref):
+            assert torch.equal(t, r), f"replay {rep}: differs from eager"
+        _ = (s0 * 2).sum().item()   # eager work between replays
