@@ -77,11 +77,17 @@ SOURCES = ("gated_delta_rule_10_amd/csrc/kda_prefill_mfma.hip", "gated_delta_rul
 
 
 def source_hash():
+    """Hash of the kernel and ABI sources without comments and blank lines, so
+    that a profile stays valid across edits that change no code."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip()).encode())
     return h.hexdigest()[:16]
 
 
@@ -95,7 +101,7 @@ def measured_traffic(profile):
     except OSError:
         return None
     want = source_hash()
-    if f"source sha256 (kda_prefill_mfma.hip, kda_decode.hip, kda_api.cpp): {want}" not in text:
+    if f"code sha256 (kda_prefill_mfma.hip, kda_decode.hip, kda_api.cpp; comments stripped): {want}" not in text:
         return None
     for line in text.splitlines():
         if line.startswith("traffic_bytes_per_launch:"):

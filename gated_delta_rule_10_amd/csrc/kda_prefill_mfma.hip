@@ -32,6 +32,12 @@
 //    scaled per value column by a power of two before its fp16 conversion, so
 //    the fp16 range never limits the magnitude of v or of the state.
 //
+// Options of kda_chunk_fwd_ex: the gates from bf16 pre-activations are formed
+// in prep as the inputs are unpacked; grouped key heads only change which q/k
+// rows prep reads; slot-indexed states only change where the state passes read
+// the initial and write the final state; the RMS-norm / output-gate epilogue
+// runs in the output pass on an fp32 tile of each chunk's outputs.
+//
 // MFMA fragment conventions (v_mfma_f32_16x16x32_f16, lane l, r = l % 16,
 // g = l / 16): A operand holds A[r][k(g, e)], B operand B[k(g, e)][r], result
 // D[4g + e'][r], e = 0..7, e' = 0..3. Along every contraction index this file
@@ -51,7 +57,6 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-
 
 constexpr int kC = 64;
 constexpr float kFastRange = 10.f;  // max decay exponent of one sub-chunk on the fp16 path
@@ -579,7 +584,8 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
 // from the identity with V = 0 and N (d_k x d_v) the segment run from zero.
 //  * seg_kernel, every segment but the last of each sequence, in parallel:
 //    segment 0 runs from the initial state (its end state enters segment 1), a
-//    middle segment runs once for M and once for N (two workgroups);
+//    middle segment runs from the identity for M and from zero for N, both in
+//    one workgroup;
 //  * prefix_kernel: S_in(g + 1) = M_g S_in(g) + N_g along the middle segments;
 //  * out_kernel, every segment in parallel from its incoming state, with outputs;
 //    the last segment of a sequence writes the final state.
