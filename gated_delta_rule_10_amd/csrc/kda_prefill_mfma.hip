@@ -99,11 +99,10 @@ struct Rec {
     static constexpr size_t KEXP = 0;                        // [i 4][cb NCB]  (K.e^G)
     static constexpr size_t QG = KEXP + 4 * NCB * FRAG;      // [i 4][cb NCB]  (Q.e^G)
     static constexpr size_t KGT = QG + 4 * NCB * FRAG;       // [ct NCT][ks 2] (K.e^{G_n-G})^T
-    static constexpr size_t TM = KGT + 2 * NCT * FRAG;       // 6 lower blocks of T
+    static constexpr size_t TM = KGT + 2 * NCT * FRAG;       // 6 lower blocks of T Diag(beta)
     static constexpr size_t PM = TM + 6 * FRAG;              // 6 lower blocks of P
     static constexpr size_t GAM = PM + 6 * FRAG;             // e^{G_n} [K] fp32
-    static constexpr size_t BET = GAM + 4 * K;               // beta [64] fp32
-    static constexpr size_t BYTES = (BET + 4 * kC + 255) / 256 * 256;
+    static constexpr size_t BYTES = (GAM + 4 * K + 255) / 256 * 256;
 };
 // (row block i, 32-wide k step ks) -> fragment index for the lower-triangular T and P
 __device__ __forceinline__ int tri(int i, int ks) { return i < 2 ? i : 2 * i - 2 + ks; }
@@ -205,8 +204,6 @@ __device__ __forceinline__ PrepItem prep_item(const PrefillArgs &a, const int32_
     return PrepItem{c, h, lo, t0, min(kC, ld_meta(a.cu_seqlens, lo + 1) - t0)};
 }
 
-// The inputs one lane reads for a work item: token 16w + r of the chunk, channels
-// 32 cb + 16 hf + 4g .. + 3 (bf16 q and k as raw pairs, log decay fp32), and beta.
 // The inputs one lane reads for a work item: token 16w + r of the chunk and, per
 // 32-channel block, the 8 consecutive channels o(g) .. o(g) + 7 with
 // o(g) = 16 (g & 1) + 8 (g >> 1), so every k, q (and bf16 gate) load is 16 bytes.
@@ -563,7 +560,7 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int col = 32 * ks + kidx(g, e);
-                tf[e] = static_cast<_Float16>(sm.u.b.T[16 * w + r][col]);
+                tf[e] = static_cast<_Float16>(sm.u.b.T[16 * w + r][col] * sm.beta[col]);
                 pf[e] = static_cast<_Float16>(sm.u.b.P[16 * w + r][col]);
             }
             *reinterpret_cast<half8 *>(rec + R::TM + (tri(w, ks) * 64 + l) * 16) = tf;
@@ -571,7 +568,6 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
         }
     }
     if (tid < K) reinterpret_cast<float *>(rec + R::GAM)[tid] = sm.fac[15][tid];
-    if (tid < kC) reinterpret_cast<float *>(rec + R::BET)[tid] = sm.beta[tid];
     __syncthreads();  // the next item rewrites the LDS this one read last
     }
 }
@@ -664,8 +660,9 @@ __device__ __forceinline__ void dma4(const void *base, uint32_t voff, const char
 
 // Copy chunk data into LDS buffer `dst`, spread over the NW waves: the record
 // fragments the pass reads (all of them with outputs, else K.e^G, its transpose
-// with e^{G_n-G}, and T), e^{G_n} and beta, and (HASV) the 64 x V tile of V.
-// Tokens past the sequence end read the last token (finite; beta is 0 there).
+// with e^{G_n-G}, and T Diag(beta)), e^{G_n}, and (HASV) the 64 x V tile of V.
+// Tokens past the sequence end read the last token (finite; their columns of
+// T Diag(beta) are zero).
 template <int K, int V, bool FULL, bool HASV, int NW>
 __device__ __forceinline__ void copy_chunk(char *dst, const char *rec, const bf16_t *vg, int t0, int tend,
                                            int H, int h, int w, int l) {
@@ -678,12 +675,12 @@ __device__ __forceinline__ void copy_chunk(char *dst, const char *rec, const bf1
         const int fi = (FULL || f < NKX) ? f : f - NKX + KG0;
         dma16(rec + fi * 1024, lo, dst + fi * 1024);
     }
-    // e^{G_n} [K] and beta [64], fp32: K + 64 words in copies of 256 B
-    static_assert(R::BET + 4 * kC == R::GAM + 256 * ((K + kC) / 64), "gamma + beta span");
+    // e^{G_n} [K] fp32 in copies of 256 B
+    static_assert(K % 64 == 0, "e^{G_n} span");
     if (w == NW - 1) {
         const uint32_t l4 = static_cast<uint32_t>(l) * 4u;
 #pragma unroll
-        for (int q = 0; q < (K + kC) / 64; ++q) dma4(rec + R::GAM + q * 256, l4, dst + R::GAM + q * 256);
+        for (int q = 0; q < K / 64; ++q) dma4(rec + R::GAM + q * 256, l4, dst + R::GAM + q * 256);
     }
     if (HASV) {
         using VT = VTile<V>;
@@ -715,9 +712,10 @@ __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F);
 
 // One chunk for one wave holding NB 16-column blocks of the state, S[j][ct] =
 // rows 16 ct + 4g + e of column col0 + 16 j + r. part_a: column scales of the
-// state, (K.e^G) S and (OUT) (Q.e^G) S, and X = Diag(beta)(V - (K.e^G) S) as
-// scaled fp16 operands (V = 0 without HASV). part_b: U' = T X, the state update
-// and (OUT) the outputs O = (Q.e^G) S + P U' of tokens 16i + 4g + e in out[j][i].
+// state, (K.e^G) S and (OUT) (Q.e^G) S, and X = V - (K.e^G) S as scaled fp16
+// operands (V = 0 without HASV). part_b: U' = (T Diag(beta)) X (beta is folded
+// into the record's T fragments), the state update and (OUT) the outputs
+// O = (Q.e^G) S + P U' of tokens 16i + 4g + e in out[j][i].
 template <int K, int V, int NB, bool OUT, bool HASV>
 struct ChunkStep {
     static constexpr int NCB = K / 32, NCT = K / 16;
@@ -772,14 +770,13 @@ struct ChunkStep {
             float mx = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const f4 bb = *reinterpret_cast<const f4 *>(buf + R::BET + (16 * i + 4 * g) * 4);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     float vv = 0.f;
                     if (HASV)
                         vv = bf16_to_f32(*reinterpret_cast<const bf16_t *>(
                             buf + ScanBuf<K, V>::VT + VTile<V>::off(16 * i + 4 * g + e, col0 + 16 * j + r)));
-                    X[i][e] = bb[e] * fmaf(-sigs[j], xa[j][i][e], vv);
+                    X[i][e] = fmaf(-sigs[j], xa[j][i][e], vv);
                     mx = fmaxf(mx, fabsf(X[i][e]));
                 }
             }
