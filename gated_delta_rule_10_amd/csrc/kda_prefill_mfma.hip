@@ -696,8 +696,19 @@ __device__ __forceinline__ void copy_chunk(char *dst, const char *rec, const bf1
 // fp32 -> bf16 bits, round to nearest even (the gfx950 conversion instruction)
 __device__ __forceinline__ bf16_t bf16_rne(float x) { return __builtin_bit_cast(bf16_t, static_cast<__bf16>(x)); }
 
-__device__ __forceinline__ half8 lds_frag(const char *buf, size_t off, int l) {
-    return *reinterpret_cast<const half8 *>(buf + off + l * 16);
+// Fragment reads of a chunk buffer go through a per-buffer lane base (the LDS
+// address of buf + 16 l) that the compiler cannot fold into constants: every
+// fragment offset inside a record is below 64 KB, so each read then takes its
+// offset from the ds_read immediate, also for the buffer that starts above 64 KB
+// (otherwise each read of that buffer needs its own address instruction).
+typedef __attribute__((address_space(3))) const char lds_cchar;
+__device__ __forceinline__ lds_cchar *frag_base(const char *buf, int l) {
+    uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)buf)) + 16u * static_cast<uint32_t>(l);
+    __asm__("" : "+v"(a));
+    return reinterpret_cast<lds_cchar *>(static_cast<uintptr_t>(a));
+}
+__device__ __forceinline__ half8 lds_frag(lds_cchar *fb, size_t off) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) half8 *>(fb + off);
 }
 
 // Workgroup barrier without a memory fence: callers wait for the counters they
@@ -724,7 +735,8 @@ struct ChunkStep {
     half8 xf[NB][2];
     f4 oa[NB][4];
 
-    __device__ __forceinline__ void part_a(const char *buf, const f4 (&S)[NB][NCT], int col0, int l, int r, int g) {
+    __device__ __forceinline__ void part_a(const char *buf, lds_cchar *fb, const f4 (&S)[NB][NCT], int col0, int l, int r,
+                                           int g) {
         half8 sf[NB][NCB];
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
@@ -755,11 +767,11 @@ struct ChunkStep {
         for (int kb = 0; kb < NCB; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const half8 kx = lds_frag(buf, R::KEXP + (i * NCB + kb) * 1024, l);
+                const half8 kx = lds_frag(fb, R::KEXP + (i * NCB + kb) * 1024);
 #pragma unroll
                 for (int j = 0; j < NB; ++j) xa[j][i] = mfma(kx, sf[j][kb], xa[j][i]);
                 if (OUT) {
-                    const half8 qx = lds_frag(buf, R::QG + (i * NCB + kb) * 1024, l);
+                    const half8 qx = lds_frag(fb, R::QG + (i * NCB + kb) * 1024);
 #pragma unroll
                     for (int j = 0; j < NB; ++j) oa[j][i] = mfma(qx, sf[j][kb], oa[j][i]);
                 }
@@ -792,11 +804,11 @@ struct ChunkStep {
         }
     }
 
-    __device__ __forceinline__ void part_b(const char *buf, f4 (&S)[NB][NCT], f4 (&out)[NB][4], float scale, int l,
-                                           int g) {
+    __device__ __forceinline__ void part_b(const char *buf, lds_cchar *fb, f4 (&S)[NB][NCT], f4 (&out)[NB][4],
+                                           float scale, int g) {
         half8 tm[6];
 #pragma unroll
-        for (int f = 0; f < 6; ++f) tm[f] = lds_frag(buf, R::TM + f * 1024, l);
+        for (int f = 0; f < 6; ++f) tm[f] = lds_frag(fb, R::TM + f * 1024);
         half8 uf[NB][2];
         float sigu[NB];
 #pragma unroll
@@ -827,8 +839,8 @@ struct ChunkStep {
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             const f4 gm = *reinterpret_cast<const f4 *>(buf + R::GAM + (16 * ct + 4 * g) * 4);
-            const half8 k0 = lds_frag(buf, R::KGT + (ct * 2 + 0) * 1024, l);
-            const half8 k1 = lds_frag(buf, R::KGT + (ct * 2 + 1) * 1024, l);
+            const half8 k0 = lds_frag(fb, R::KGT + (ct * 2 + 0) * 1024);
+            const half8 k1 = lds_frag(fb, R::KGT + (ct * 2 + 1) * 1024);
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 const f4 acc = mfma(k1, uf[j][1], mfma(k0, uf[j][0], zero4()));
@@ -840,9 +852,9 @@ struct ChunkStep {
             // O = (Q.e^G) S + P U'
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const half8 p0 = lds_frag(buf, R::PM + tri(i, 0) * 1024, l);
+                const half8 p0 = lds_frag(fb, R::PM + tri(i, 0) * 1024);
                 half8 p1 = p0;
-                if (i >= 2) p1 = lds_frag(buf, R::PM + tri(i, 1) * 1024, l);
+                if (i >= 2) p1 = lds_frag(fb, R::PM + tri(i, 1) * 1024);
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
                     f4 pu = mfma(p0, uf[j][0], zero4());
@@ -957,7 +969,8 @@ __device__ __forceinline__ void run_segment(char *lb0, char *lb1, char *ftd, f4 
         }
     };
 
-    auto body = [&](char *cur, char *oth, int c) {
+    lds_cchar *const fb0 = frag_base(lb0, l), *const fb1 = frag_base(lb1, l);
+    auto body = [&](char *cur, lds_cchar *fbc, char *oth, int c) {
         const int tc = tbeg + (c - cb) * kC;
         wait_all();  // this wave's copies of chunk c, its stores and its LDS writes are done
         wg_barrier();
@@ -1002,9 +1015,9 @@ __device__ __forceinline__ void run_segment(char *lb0, char *lb1, char *ftd, f4 
             }
         }
         ChunkStep<K, V, NB, OUT, HASV> st;
-        if (active) st.part_a(cur, S, col0, l, r, g);
+        if (active) st.part_a(cur, fbc, S, col0, l, r, g);
         if (TILE) wg_barrier();  // every wave has read K.e^G, Q.e^G and V of chunk c: the tile may go there
-        if (active) st.part_b(cur, S, out, scale, l, g);
+        if (active) st.part_b(cur, fbc, S, out, scale, g);
         if (OUT && active) {
 #pragma unroll
             for (int j = 0; j < NB; ++j)
@@ -1027,9 +1040,9 @@ __device__ __forceinline__ void run_segment(char *lb0, char *lb1, char *ftd, f4 
     // two chunks per iteration, so that each buffer is a distinct LDS object: copies
     // into one never make reads of the other wait
     for (int c = cb; c < ce; c += 2) {
-        body(lb0, lb1, c);
+        body(lb0, fb0, lb1, c);
         if (c + 1 >= ce) break;
-        body(lb1, lb0, c + 1);
+        body(lb1, fb1, lb0, c + 1);
     }
     if (TILE) {
         wait_all();
