@@ -974,7 +974,7 @@ __device__ __forceinline__ void run_segment(char *lb0, char *lb1, char *ftd, f4 
         const int tc = tbeg + (c - cb) * kC;
         wait_all();  // this wave's copies of chunk c, its stores and its LDS writes are done
         wg_barrier();
-        u4 pc[EPI ? 1 : NP];
+        u4 pc[(EPI || NP == 0) ? 1 : NP];
         f4 fx[4];
         if (TILE && c > cb) {
             if (EPI) {
@@ -1126,11 +1126,12 @@ struct SegBufs {
 // idle on segment 0, and issue all the chunk copies (their products are the
 // lighter ones); the others carry N (from zero), or on segment 0 the state from
 // the initial state.
+constexpr int kSegNB = 1;  // 16-column blocks per wave in the map pass
 template <int K, int V>
-__global__ __launch_bounds__(64 * (K + V) / 32) void seg_kernel(PrefillArgs a, const int32_t *off,
-                                                                const int32_t *soff, int L, const char *recs,
-                                                                SegBufs sb) {
-    constexpr int NW = (K + V) / 32, WM = K / 32, NB = 2;
+__global__ __launch_bounds__(64 * (K + V) / (16 * kSegNB)) void seg_kernel(PrefillArgs a, const int32_t *off,
+                                                                           const int32_t *soff, int L,
+                                                                           const char *recs, SegBufs sb) {
+    constexpr int NB = kSegNB, NW = (K + V) / (16 * NB), WM = K / (16 * NB);
     __shared__ __attribute__((aligned(16))) char lb0[ScanBuf<K, V>::BYTES];
     __shared__ __attribute__((aligned(16))) char lb1[ScanBuf<K, V>::BYTES];
     const int H = a.H;
@@ -1147,7 +1148,7 @@ __global__ __launch_bounds__(64 * (K + V) / 32) void seg_kernel(PrefillArgs a, c
     const size_t skv = (static_cast<size_t>(s) * H + h) * K * V;
     f4 S[NB][K / 16];
     if (w < WM) {
-        const int col0 = 32 * w;
+        const int col0 = 16 * NB * w;
 #pragma unroll
         for (int j = 0; j < NB; ++j)
 #pragma unroll
@@ -1159,7 +1160,7 @@ __global__ __launch_bounds__(64 * (K + V) / 32) void seg_kernel(PrefillArgs a, c
                                                                         si.gl > 0, tid, w, l, r, g, col0);
         if (si.gl > 0) store_state<K, NB>(S, sb.mapm + (static_cast<size_t>(s) * H + h) * K * K, K, col0, r, g);
     } else {
-        const int col0 = 32 * (w - WM);
+        const int col0 = 16 * NB * (w - WM);
         const float *init = si.gl == 0 ? state_in(a, si.n, h) : nullptr;
         load_state<K, NB>(S, init, V, col0, r, g);
         // segment 0: a copy of the initial state for the output pass (final_state may alias it)
@@ -1318,7 +1319,7 @@ hipError_t launch_kv(const PrefillArgs &a, hipStream_t st) {
     const int64_t maxc = (static_cast<int64_t>(a.T) + kC - 1) / kC;
     const size_t units = lay.nseg * a.H;
     if (maxc > lay.L) {
-        hipLaunchKernelGGL((seg_kernel<K, V>), dim3(static_cast<unsigned>(units)), dim3(64 * (K + V) / 32), 0, st, a,
+        hipLaunchKernelGGL((seg_kernel<K, V>), dim3(static_cast<unsigned>(units)), dim3(64 * (K + V) / (16 * kSegNB)), 0, st, a,
                            off, soff, lay.L, recs, sb);
         if (maxc > 2 * static_cast<int64_t>(lay.L))
             hipLaunchKernelGGL((prefix_kernel<K, V>), dim3(static_cast<unsigned>(a.N) * a.H * (V / 16)), dim3(256), 0,
