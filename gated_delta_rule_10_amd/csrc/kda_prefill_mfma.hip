@@ -585,9 +585,9 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
 //  * prefix_kernel: S_in(g + 1) = M_g S_in(g) + N_g along the middle segments;
 //  * out_kernel, every segment in parallel from its incoming state, with outputs;
 //    the last segment of a sequence writes the final state.
-// A workgroup covers all columns of one (segment, head) state (and of M), two
-// waves per SIMD; each wave holds 16 or 32 columns x d_k rows in MFMA
-// accumulators. A chunk's record is copied global -> LDS once per workgroup with
+// A workgroup covers all columns of one (segment, head) state (and of M); each
+// wave holds 16 columns x d_k rows in MFMA accumulators (four waves per SIMD in
+// the map pass, two in the output pass). A chunk's record is copied global -> LDS once per workgroup with
 // direct-to-LDS loads, one chunk ahead, into a two-buffer ring, so that no record
 // is streamed by more than one compute unit at a time; while one wave of a SIMD
 // waits on the memory pipeline the other computes.
@@ -1121,11 +1121,11 @@ struct SegBufs {
     float *mapn;  // [segments, H, d_k, d_v] N of middle segments
 };
 
-// One workgroup per (segment, head), (d_k + d_v) / 32 waves of 32 columns: the
-// first d_k / 32 waves carry M (from the identity, V = 0) of a middle segment and
+// One workgroup per (segment, head), (d_k + d_v) / 16 waves of 16 columns: the
+// first d_k / 16 waves carry M (from the identity, V = 0) of a middle segment and
 // idle on segment 0, and issue all the chunk copies (their products are the
-// lighter ones); the others carry N (from zero), or on segment 0 the state from
-// the initial state.
+// lighter ones: letting every wave copy makes the pass slower); the others carry
+// N (from zero), or on segment 0 the state from the initial state.
 constexpr int kSegNB = 1;  // 16-column blocks per wave in the map pass
 template <int K, int V>
 __global__ __launch_bounds__(64 * (K + V) / (16 * kSegNB)) void seg_kernel(PrefillArgs a, const int32_t *off,
