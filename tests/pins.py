@@ -324,10 +324,44 @@ def pin_contraction_bound(oracle):
         prev = cur
 
 
+def load_worked_example(name="worked_3tok_dk2.json"):
+    """A hand-derived example under tests/golden/ (exact fractions), as arrays:
+    q, k, v, log_alpha [T, 1, dim], beta [T, 1], initial state [1, 1, K, V],
+    expected o [T, 1, V] and final state [1, 1, K, V]."""
+    import json
+    import os
+    from fractions import Fraction
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", name)
+    with open(path, encoding="utf-8") as f:
+        ex = json.load(f)
+    num = lambda x: float(Fraction(x))
+    toks = ex["tokens"]
+    arr = lambda key: np.array([[num(x) for x in t[key]] for t in toks])[:, None, :]
+    beta = np.array([[num(t["beta"])] for t in toks])
+    s0 = np.array([[num(x) for x in row] for row in ex["initial_state"]])[None, None]
+    o = np.array([[num(x) for x in row] for row in ex["expected"]["o"]])[:, None, :]
+    sT = np.array([[num(x) for x in row] for row in ex["expected"]["final_state"]])[None, None]
+    return arr("q"), arr("k"), arr("v"), np.log(arr("alpha")), beta, s0, o, sT
+
+
+def pin_worked_example(oracle):
+    """Prefill and decode reproduce the hand-derived worked example (the gates
+    reach the oracle as fp32 log alpha: compared to a few fp32 ulps)."""
+    q, k, v, g, b, s0, o_ref, s_ref = load_worked_example()
+    T = q.shape[0]
+    o, sT = oracle.prefill(q, k, v, g, b, [0, T], 1.0, s0)
+    assert np.abs(o - o_ref).max() < 1e-6 and np.abs(sT - s_ref).max() < 1e-6
+    state = np.ascontiguousarray(s0[0][None], dtype=np.float64)
+    for t in range(T):
+        od = oracle.decode(q[t:t + 1], k[t:t + 1], v[t:t + 1], g[t:t + 1], b[t:t + 1], state)
+        assert np.abs(od[0] - o_ref[t]).max() < 1e-6
+    assert np.abs(state - s_ref).max() < 1e-6
+
+
 ALL_PINS = [
     pin_single_token_zero_state, pin_scale, pin_zero_write, pin_pure_decay,
     pin_exact_retrieval, pin_overwrite, pin_dense_transition_products,
     pin_gated_deltanet_orientation, pin_scalar_key, pin_linearity,
     pin_state_split, pin_varlen_equals_separate, pin_decode_equals_prefill,
-    pin_decode_closed_forms, pin_contraction_bound,
+    pin_decode_closed_forms, pin_contraction_bound, pin_worked_example,
 ]
