@@ -109,6 +109,17 @@ def measured_traffic(profile):
     return None
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def _cpu_threads():
     env = os.environ.get("OMP_NUM_THREADS")
     if env and env.isdigit():
@@ -134,7 +145,7 @@ def cpu_baseline_prefill(d, target_s=12.0):
         if elapsed >= target_s / 2 or tokens >= d["q"].shape[0]:
             break
         tokens = min(d["q"].shape[0], int(tokens * max(2.0, min(16.0, target_s / max(elapsed, 1e-3)))))
-    return dict(value=tokens / elapsed / 1e6, unit="Mtokens/s", cores=threads, kind="oracle",
+    return dict(value=tokens / elapsed / 1e6, unit="Mtokens/s", cores=threads, cpu=_cpu_model(), kind="oracle",
                 sample=f"fp64 oracle, first {tokens} tokens of the 128K sequence, all 32 heads, "
                        f"{elapsed:.2f} s", seconds=elapsed)
 
@@ -150,7 +161,7 @@ def cpu_baseline_decode(d, steps=3):
         oracle.decode(host["q"][s], host["k"][s], host["v"][s], host["log_alpha"][s],
                       host["beta"][s], state, nthreads=threads)
     el = time.perf_counter() - t0
-    return dict(value=el / steps * 1e6, unit="us/step", cores=threads, kind="oracle",
+    return dict(value=el / steps * 1e6, unit="us/step", cores=threads, cpu=_cpu_model(), kind="oracle",
                 sample=f"fp64 oracle, {steps} decode steps of B=64, H=32, d=128")
 
 
@@ -281,6 +292,33 @@ def main():
     if not args.no_cpu_baseline:
         cpu_d = {n: d[n] for n in ("q", "k", "v", "log_alpha", "beta", "initial_state")}
     del d, o, sT
+
+    # ---- the same operator on one 1,048,576-token sequence (the pages' 1M point)
+    if not args.no_variants:
+        torch.cuda.empty_cache()
+        d1 = inputs.device_workload_inputs("long_1m", device=dev)
+        T1 = d1["q"].shape[0]
+        o1 = torch.empty((T1, H, V), dtype=torch.bfloat16, device=dev)
+        s1 = torch.empty((1, H, K, V), dtype=torch.float32, device=dev)
+        ws1 = torch.empty(kda.kda_chunk_fwd_workspace_size(1, T1, H, K, V, torch.bfloat16), dtype=torch.uint8,
+                          device=dev)
+
+        def step1m():
+            kda.kda_chunk_fwd(d1["q"], d1["k"], d1["v"], d1["log_alpha"], d1["beta"], d1["cu_seqlens"],
+                              initial_state=d1["initial_state"], final_state=s1, o=o1, workspace=ws1,
+                              stream=stream)
+
+        ms1 = time_calls(step1m, 3, 1, stream)
+        b1 = prefill_bytes(T1, H, K, V, 1)
+        g1 = b1 / (ms1 / 1e3) / 1e9
+        result["variants"]["long_1m"] = {
+            "entry": "kda_chunk_fwd", "workload": "1 sequence x 1048576 tokens, H=32, d_k=d_v=128, bf16, "
+                                                  "log alpha = -0.05 softplus(x), random initial state",
+            "ms_per_step": round(ms1, 3), "value": round(T1 / (ms1 / 1e3) / 1e6, 3), "unit": "Mtokens/s",
+            "roofline": {"bound": "hbm", "achieved": round(g1, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(g1 / PEAK_HBM_GBS, 4), "algorithmic_bytes_per_launch": b1}}
+        del d1, o1, s1, ws1
+        torch.cuda.empty_cache()
 
     # ---- decode: 64 sequences x 32 heads, fp32 cache -----------------------
     if not args.prefill_only:

@@ -229,6 +229,9 @@ WORKLOADS = {
                         V=128, in_dtype="bf16", decay_scale=0.1,
                         init="odd_zero", n_seqs=16, len_lo=1024,
                         len_hi=65536, total=524288),
+    # the 1M-token point of the pages' long-context figures (timed only)
+    "long_1m": dict(kind="prefill", seed=5, lengths=[1048576], H=32, K=128,
+                    V=128, in_dtype="bf16", decay_scale=0.05, init="random"),
 }
 
 
