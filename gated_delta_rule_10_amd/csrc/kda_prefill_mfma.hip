@@ -46,6 +46,7 @@
 // product's result feeds the next product's B operand from registers.
 #include <algorithm>
 #include <cstdlib>
+#include <mutex>
 #include <type_traits>
 
 #include "kda_device.h"
@@ -1163,14 +1164,26 @@ __global__ __launch_bounds__(64 * (K + V) / (16 * kSegNB)) void seg_kernel(Prefi
         const int col0 = 16 * NB * (w - WM);
         const float *init = si.gl == 0 ? state_in(a, si.n, h) : nullptr;
         load_state<K, NB>(S, init, V, col0, r, g);
-        // segment 0: a copy of the initial state for the output pass (final_state may alias it)
-        if (si.gl == 0) store_state<K, NB>(S, sb.sin + skv, V, col0, r, g);
         run_segment<K, V, NB, false, true, true, NW, WM, false, float>(lb0, lb1, nullptr, S, hrec, cb, ce, tbeg, tend,
                                                                        vg, nullptr, H, h, 1.f, Epi{}, true, tid, w,
                                                                        l, r, g, col0);
         store_state<K, NB>(S, si.gl == 0 ? sb.sin + skv + static_cast<size_t>(H) * K * V : sb.mapn + skv, V, col0, r,
                            g);
     }
+}
+
+// For a sequence cut into several segments: a copy of its initial state (zeros
+// without one) as the incoming state of its segment 0, which the output pass
+// reads. The output pass writes final states (which may alias the initial
+// states) while other segments of it still run, and its segment-0 workgroups may
+// run beside the map pass, so they read this copy.
+template <int K, int V>
+__global__ __launch_bounds__(256) void seed_kernel(PrefillArgs a, const int32_t *soff, SegBufs sb) {
+    const int n = blockIdx.x / a.H, h = blockIdx.x - (blockIdx.x / a.H) * a.H;
+    if (n >= a.N || soff[n + 1] - soff[n] < 2) return;
+    const float4 *src = reinterpret_cast<const float4 *>(state_in(a, n, h));
+    float4 *dst = reinterpret_cast<float4 *>(sb.sin + (static_cast<size_t>(soff[n]) * a.H + h) * K * V);
+    for (int i = threadIdx.x; i < K * V / 4; i += 256) dst[i] = src ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 // S_in(g + 1) = M_g S_in(g) + N_g for the middle segments g of one (sequence, head),
@@ -1221,9 +1234,10 @@ __global__ __launch_bounds__(256) void prefix_kernel(const int32_t *soff, int N,
     }
 }
 
+// pass: 0 = only the segments 0 of their sequences, 1 = only the others, 2 = all
 template <int K, int V, typename TOut, bool EPI>
 __global__ __launch_bounds__(64 * V / 16) void out_kernel(PrefillArgs a, const int32_t *off, const int32_t *soff,
-                                                          int L, const char *recs, SegBufs sb) {
+                                                          int L, const char *recs, SegBufs sb, int pass) {
     constexpr int NB = 1, NW = V / 16;
     // the fp32 epilogue tile goes into the K.e^G / Q.e^G region of a chunk buffer when it fits
     constexpr bool FTD = EPI && static_cast<size_t>(kC) * V * 4 > Rec<K>::KGT;
@@ -1234,6 +1248,7 @@ __global__ __launch_bounds__(64 * V / 16) void out_kernel(PrefillArgs a, const i
     const int s = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
     if (s >= soff[a.N]) return;
     const SegInfo si = seg_of(soff, a.N, s);
+    if ((pass == 0 && si.gl != 0) || (pass == 1 && si.gl == 0)) return;
     const int tid = threadIdx.x, l = tid & 63, r = l & 15, g = l >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col0 = 16 * NB * w;
@@ -1295,6 +1310,51 @@ struct WsLayout {
     }
 };
 
+// A second stream per device, with the events that fork it from and join it to
+// the caller's stream: the output pass of the segments 0 runs on it beside the
+// map pass, on the compute units the map pass leaves free (one workgroup per
+// middle segment and head). Created on first use, at default priority; calls
+// hold the lock while they enqueue, so the fork and join of concurrent callers
+// do not interleave. KDA_NO_SIDE_STREAM=1 keeps everything on the caller's stream.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    bool ok = false, tried = false;
+};
+std::mutex g_side_mu;
+SideStream *side_stream() {
+    static SideStream per_dev[64];
+    static const bool off = [] {
+        const char *e = std::getenv("KDA_NO_SIDE_STREAM");
+        return e && std::atoi(e) != 0;
+    }();
+    int dev = 0;
+    if (off || hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    SideStream &ss = per_dev[dev];
+    if (!ss.tried) {
+        ss.tried = true;
+        ss.ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess &&
+                hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess &&
+                hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
+    }
+    return ss.ok ? &ss : nullptr;
+}
+
+template <int K, int V>
+hipError_t launch_out(const PrefillArgs &a, const int32_t *off, const int32_t *soff, int L, const char *recs,
+                      const SegBufs &sb, size_t units, int pass, hipStream_t st) {
+    const dim3 og(static_cast<unsigned>(units)), ob(64 * V / 16);
+    const bool epi = a.norm || a.z;
+    if (a.out_dtype == KDA_BF16) {
+        if (epi) hipLaunchKernelGGL((out_kernel<K, V, bf16_t, true>), og, ob, 0, st, a, off, soff, L, recs, sb, pass);
+        else hipLaunchKernelGGL((out_kernel<K, V, bf16_t, false>), og, ob, 0, st, a, off, soff, L, recs, sb, pass);
+    } else {
+        if (epi) hipLaunchKernelGGL((out_kernel<K, V, float, true>), og, ob, 0, st, a, off, soff, L, recs, sb, pass);
+        else hipLaunchKernelGGL((out_kernel<K, V, float, false>), og, ob, 0, st, a, off, soff, L, recs, sb, pass);
+    }
+    return hipGetLastError();
+}
+
 template <int K, int V>
 hipError_t launch_kv(const PrefillArgs &a, hipStream_t st) {
     const WsLayout<K, V> lay(a.N, a.T, a.H);
@@ -1318,23 +1378,26 @@ hipError_t launch_kv(const PrefillArgs &a, hipStream_t st) {
     // every sequence has at most ceil(T / 64) chunks: one segment if that fits in L
     const int64_t maxc = (static_cast<int64_t>(a.T) + kC - 1) / kC;
     const size_t units = lay.nseg * a.H;
-    if (maxc > lay.L) {
-        hipLaunchKernelGGL((seg_kernel<K, V>), dim3(static_cast<unsigned>(units)), dim3(64 * (K + V) / (16 * kSegNB)), 0, st, a,
-                           off, soff, lay.L, recs, sb);
-        if (maxc > 2 * static_cast<int64_t>(lay.L))
-            hipLaunchKernelGGL((prefix_kernel<K, V>), dim3(static_cast<unsigned>(a.N) * a.H * (V / 16)), dim3(256), 0,
-                               st, soff, a.N, a.H, sb);
+    if (maxc <= lay.L) return launch_out<K, V>(a, off, soff, lay.L, recs, sb, units, 2, st);
+
+    hipLaunchKernelGGL((seed_kernel<K, V>), dim3(static_cast<unsigned>(a.N) * a.H), dim3(256), 0, st, a, soff, sb);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    SideStream *side = side_stream();
+    if (side) {  // segments 0 of the output pass beside the map pass
+        if ((e = hipEventRecord(side->fork, st)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess) return e;
+        if ((e = launch_out<K, V>(a, off, soff, lay.L, recs, sb, units, 0, side->s)) != hipSuccess) return e;
+        if ((e = hipEventRecord(side->join, side->s)) != hipSuccess) return e;
     }
-    const dim3 og(static_cast<unsigned>(units)), ob(64 * V / 16);
-    const bool epi = a.norm || a.z;
-    if (a.out_dtype == KDA_BF16) {
-        if (epi) hipLaunchKernelGGL((out_kernel<K, V, bf16_t, true>), og, ob, 0, st, a, off, soff, lay.L, recs, sb);
-        else hipLaunchKernelGGL((out_kernel<K, V, bf16_t, false>), og, ob, 0, st, a, off, soff, lay.L, recs, sb);
-    } else {
-        if (epi) hipLaunchKernelGGL((out_kernel<K, V, float, true>), og, ob, 0, st, a, off, soff, lay.L, recs, sb);
-        else hipLaunchKernelGGL((out_kernel<K, V, float, false>), og, ob, 0, st, a, off, soff, lay.L, recs, sb);
-    }
-    return hipGetLastError();
+    hipLaunchKernelGGL((seg_kernel<K, V>), dim3(static_cast<unsigned>(units)), dim3(64 * (K + V) / (16 * kSegNB)), 0,
+                       st, a, off, soff, lay.L, recs, sb);
+    if (maxc > 2 * static_cast<int64_t>(lay.L))
+        hipLaunchKernelGGL((prefix_kernel<K, V>), dim3(static_cast<unsigned>(a.N) * a.H * (V / 16)), dim3(256), 0, st,
+                           soff, a.N, a.H, sb);
+    if ((e = launch_out<K, V>(a, off, soff, lay.L, recs, sb, units, side ? 1 : 2, st)) != hipSuccess) return e;
+    if (side) e = hipStreamWaitEvent(st, side->join, 0);
+    return e;
 }
 
 }  // namespace
@@ -1347,6 +1410,7 @@ size_t prefill_mfma_workspace(int32_t N, int32_t T, int32_t H, int32_t K, int32_
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t st) {
+    const std::lock_guard<std::mutex> lock(g_side_mu);  // one enqueue sequence at a time (shared side stream)
     if (a.K == 128 && a.V == 128) return launch_kv<128, 128>(a, st);
     if (a.K == 128 && a.V == 64) return launch_kv<128, 64>(a, st);
     if (a.K == 64 && a.V == 128) return launch_kv<64, 128>(a, st);
