@@ -24,8 +24,15 @@
  *
  * Conventions shared by every entry point
  *  - Every pointer argument is DEVICE memory on the current HIP device,
- *    owned by the caller. The library never allocates, frees or
- *    synchronises; all work is enqueued on `stream` and runs asynchronously.
+ *    owned by the caller. The library never allocates or frees device memory
+ *    and never synchronises; the work runs asynchronously, ordered on `stream`.
+ *    The prefill entry points may run part of a call on a second stream of
+ *    the library's own (one per device, created with two events at the first
+ *    call that needs it, default priority, kept until the process ends),
+ *    forked from and joined back to `stream` with those events: the call as a
+ *    whole is still ordered on `stream`, and can be captured in a HIP graph
+ *    (the first call should then come before the capture). KDA_NO_SIDE_STREAM=1
+ *    in the environment keeps all work on `stream`.
  *  - Every pointer must be 16-byte aligned; tensors are dense, row-major,
  *    with the layouts given below (last dimension contiguous).
  *  - Arguments are validated on the host before anything is enqueued. A
@@ -35,8 +42,9 @@
  *    cu_seqlens must be non-decreasing from 0 to T_total, log_alpha finite
  *    and <= 0, slot indices distinct and in range. Stability of the
  *    recurrence needs ||k_t|| <= 1 and beta_t in [0, 2].
- *  - Functions hold no global mutable state and are re-entrant; calls on
- *    different streams that write the same memory race.
+ *  - Apart from that stream and its events, the library holds no global
+ *    mutable state. Calls are thread-safe (prefill calls take a lock while
+ *    they enqueue); calls on different streams that write the same memory race.
  *  - No C++ exception crosses this interface.
  */
 #ifndef KDA_H_
