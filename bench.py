@@ -249,7 +249,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic("prefill_long_128k.md"),
-                     "kernel": "kda_chunk_fwd (one call: offsets, prep, map pass, prefix, output pass)",
+                     "kernel": "kda_chunk_fwd (one call: offsets, initial-state copies, prep, map pass, prefix, output pass)",
                      "algorithmic_bytes_per_launch": nbytes},
         "mfma": {"achieved_tflops": round(tflops, 2), "peak_tflops": PEAK_BF16_TFLOPS,
                  "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
