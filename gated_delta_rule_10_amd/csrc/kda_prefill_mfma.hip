@@ -66,6 +66,11 @@ __device__ __forceinline__ f4 mfma(half8 a, half8 b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f4 zero4() { return f4{0.f, 0.f, 0.f, 0.f}; }
+// Stores of data that is read at most once more, by a later pass (chunk records)
+// or not at all by this library (outputs): nontemporal, so they stream past the
+// caches instead of evicting lines that are still in use.
+template <typename T>
+__device__ __forceinline__ void store_stream(T *p, T v) { __builtin_nontemporal_store(v, p); }
 __device__ __forceinline__ int kidx(int g, int e) { return e < 4 ? 4 * g + e : 12 + 4 * g + e; }
 
 template <int SH>
@@ -419,8 +424,8 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
             cv2[e] = static_cast<_Float16>(kt * f2[e]);                 // i = w + 2
             cv3[e] = static_cast<_Float16>(kt * f3[e]);                 // i = 3 (w = 0)
         }
-        *reinterpret_cast<half8 *>(rec + R::KEXP + ((w * NCB + cb) * 64 + l) * 16) = kexp;
-        *reinterpret_cast<half8 *>(rec + R::QG + ((w * NCB + cb) * 64 + l) * 16) = qg;
+        store_stream(reinterpret_cast<half8 *>(rec + R::KEXP + ((w * NCB + cb) * 64 + l) * 16), kexp);
+        store_stream(reinterpret_cast<half8 *>(rec + R::QG + ((w * NCB + cb) * 64 + l) * 16), qg);
         sm.u.a.colv[vblk(w, w)][cb][l] = cv0;
         if (w + 1 < 4) sm.u.a.colv[vblk(w + 1, w)][cb][l] = cv1;
         if (w + 2 < 4) sm.u.a.colv[vblk(w + 2, w)][cb][l] = cv2;
@@ -440,7 +445,7 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
         half8 v;
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = sm.u.a.kgT[16 * ct + r][32 * ks + kidx(g, e)];
-        *reinterpret_cast<half8 *>(rec + R::KGT + (f * 64 + l) * 16) = v;
+        store_stream(reinterpret_cast<half8 *>(rec + R::KGT + (f * 64 + l) * 16), v);
     }
 
     // ---- pairwise products for row block w: A_wj, P_wj, j <= w
@@ -564,11 +569,11 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
                 tf[e] = static_cast<_Float16>(sm.u.b.T[16 * w + r][col] * sm.beta[col]);
                 pf[e] = static_cast<_Float16>(sm.u.b.P[16 * w + r][col]);
             }
-            *reinterpret_cast<half8 *>(rec + R::TM + (tri(w, ks) * 64 + l) * 16) = tf;
-            *reinterpret_cast<half8 *>(rec + R::PM + (tri(w, ks) * 64 + l) * 16) = pf;
+            store_stream(reinterpret_cast<half8 *>(rec + R::TM + (tri(w, ks) * 64 + l) * 16), tf);
+            store_stream(reinterpret_cast<half8 *>(rec + R::PM + (tri(w, ks) * 64 + l) * 16), pf);
         }
     }
-    if (tid < K) reinterpret_cast<float *>(rec + R::GAM)[tid] = sm.fac[15][tid];
+    if (tid < K) store_stream(reinterpret_cast<float *>(rec + R::GAM) + tid, sm.fac[15][tid]);
     __syncthreads();  // the next item rewrites the LDS this one read last
     }
 }
@@ -636,9 +641,10 @@ __device__ __forceinline__ uint64_t uniform_addr(const void *p) {
 // warning only says it will not save and restore M0 around them)
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+// Record reads (dma16, dma4) are nontemporal: a pass reads each record byte once.
 // 16 bytes per lane from uniform base + per-lane 32-bit offset
 __device__ __forceinline__ void dma16(const void *base, uint32_t voff, const char *lds) {
-    __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+    __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
                      :
                      : "s"(lds_addr(lds)), "v"(voff), "s"(uniform_addr(base))
                      : "memory", "m0");
@@ -652,7 +658,7 @@ __device__ __forceinline__ void dma16v(const void *addr, const char *lds) {
 }
 // 4 bytes per lane, 64 lanes = 256 B, uniform base + 4 lane
 __device__ __forceinline__ void dma4(const void *base, uint32_t voff, const char *lds) {
-    __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+    __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2 nt"
                      :
                      : "s"(lds_addr(lds)), "v"(voff), "s"(uniform_addr(base))
                      : "memory", "m0");
@@ -1002,7 +1008,7 @@ __device__ __forceinline__ void run_segment(char *lb0, char *lb1, char *ftd, f4 
                     const int p = q * NT + tid, row = p / (2 * V / 16), pi = p % (2 * V / 16);
                     const int tok = tc - kC + row;
                     if (tok < tend)
-                        *reinterpret_cast<u4 *>(og + (static_cast<size_t>(tok) * H + h) * V + pi * 8) = pc[q];
+                        store_stream(reinterpret_cast<u4 *>(og + (static_cast<size_t>(tok) * H + h) * V + pi * 8), pc[q]);
                 }
             }
         }
@@ -1060,7 +1066,7 @@ __device__ __forceinline__ void run_segment(char *lb0, char *lb1, char *ftd, f4 
                 const int p = q * NT + tid, row = p / (2 * V / 16), pi = p % (2 * V / 16);
                 const int tok = t0 + row;
                 const u4 v = *reinterpret_cast<const u4 *>(last + ScanBuf<K, V>::VT + VT::off(row, pi * 8));
-                if (tok < tend) *reinterpret_cast<u4 *>(og + (static_cast<size_t>(tok) * H + h) * V + pi * 8) = v;
+                if (tok < tend) store_stream(reinterpret_cast<u4 *>(og + (static_cast<size_t>(tok) * H + h) * V + pi * 8), v);
             }
         }
     }
