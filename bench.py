@@ -165,6 +165,42 @@ def cpu_baseline_decode(d, steps=3):
                 sample=f"fp64 oracle, {steps} decode steps of B=64, H=32, d=128")
 
 
+def time_prefill_workload(name, steps, warmup, dev, stream):
+    """Median time of kda_chunk_fwd on a named synthetic workload (inputs resident on the device)."""
+    import torch
+    from gated_delta_rule_10_amd import inputs, kda
+
+    torch.cuda.empty_cache()
+    w = inputs.WORKLOADS[name]
+    d1 = inputs.device_workload_inputs(name, device=dev)
+    T1, H1 = d1["q"].shape[0], d1["q"].shape[1]
+    K1, V1 = d1["q"].shape[2], d1["v"].shape[2]
+    N1 = d1["cu_seqlens"].numel() - 1
+    o1 = torch.empty((T1, H1, V1), dtype=torch.bfloat16, device=dev)
+    s1 = torch.empty((N1, H1, K1, V1), dtype=torch.float32, device=dev)
+    ws1 = torch.empty(kda.kda_chunk_fwd_workspace_size(N1, T1, H1, K1, V1, torch.bfloat16), dtype=torch.uint8,
+                      device=dev)
+
+    def call():
+        kda.kda_chunk_fwd(d1["q"], d1["k"], d1["v"], d1["log_alpha"], d1["beta"], d1["cu_seqlens"],
+                          initial_state=d1["initial_state"], final_state=s1, o=o1, workspace=ws1, stream=stream)
+
+    ms1 = time_calls(call, steps, warmup, stream)
+    b1 = prefill_bytes(T1, H1, K1, V1, N1, s0=d1["initial_state"] is not None)
+    g1 = b1 / (ms1 / 1e3) / 1e9
+    lens = d1["cu_seqlens"].diff().tolist()
+    del d1, o1, s1, ws1
+    torch.cuda.empty_cache()
+    return {
+        "entry": "kda_chunk_fwd",
+        "workload": f"{name}: {N1} sequence(s), {T1} tokens (lengths {min(lens)}-{max(lens)}), H={H1}, "
+                    f"d_k={K1}, d_v={V1}, bf16, log alpha = -{w['decay_scale']} softplus(x), "
+                    f"initial state {w['init']}",
+        "ms_per_step": round(ms1, 3), "value": round(T1 / (ms1 / 1e3) / 1e6, 3), "unit": "Mtokens/s",
+        "roofline": {"bound": "hbm", "achieved": round(g1, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(g1 / PEAK_HBM_GBS, 4), "algorithmic_bytes_per_launch": b1}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -293,32 +329,12 @@ def main():
         cpu_d = {n: d[n] for n in ("q", "k", "v", "log_alpha", "beta", "initial_state")}
     del d, o, sT
 
-    # ---- the same operator on one 1,048,576-token sequence (the pages' 1M point)
+    # ---- the same operator on the other prefill workloads: one 1,048,576-token
+    # sequence (the pages' 1M point), 16 packed sequences of mixed lengths, and
+    # 4 x 4,096 tokens at H = 16
     if not args.no_variants:
-        torch.cuda.empty_cache()
-        d1 = inputs.device_workload_inputs("long_1m", device=dev)
-        T1 = d1["q"].shape[0]
-        o1 = torch.empty((T1, H, V), dtype=torch.bfloat16, device=dev)
-        s1 = torch.empty((1, H, K, V), dtype=torch.float32, device=dev)
-        ws1 = torch.empty(kda.kda_chunk_fwd_workspace_size(1, T1, H, K, V, torch.bfloat16), dtype=torch.uint8,
-                          device=dev)
-
-        def step1m():
-            kda.kda_chunk_fwd(d1["q"], d1["k"], d1["v"], d1["log_alpha"], d1["beta"], d1["cu_seqlens"],
-                              initial_state=d1["initial_state"], final_state=s1, o=o1, workspace=ws1,
-                              stream=stream)
-
-        ms1 = time_calls(step1m, 3, 1, stream)
-        b1 = prefill_bytes(T1, H, K, V, 1)
-        g1 = b1 / (ms1 / 1e3) / 1e9
-        result["variants"]["long_1m"] = {
-            "entry": "kda_chunk_fwd", "workload": "1 sequence x 1048576 tokens, H=32, d_k=d_v=128, bf16, "
-                                                  "log alpha = -0.05 softplus(x), random initial state",
-            "ms_per_step": round(ms1, 3), "value": round(T1 / (ms1 / 1e3) / 1e6, 3), "unit": "Mtokens/s",
-            "roofline": {"bound": "hbm", "achieved": round(g1, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(g1 / PEAK_HBM_GBS, 4), "algorithmic_bytes_per_launch": b1}}
-        del d1, o1, s1, ws1
-        torch.cuda.empty_cache()
+        for wname, wsteps, wwarm in (("long_1m", 3, 1), ("varlen_512k", 5, 2), ("mid_4x4k", 20, 3)):
+            result["variants"][wname] = time_prefill_workload(wname, wsteps, wwarm, dev, stream)
 
     # ---- decode: 64 sequences x 32 heads, fp32 cache -----------------------
     if not args.prefill_only:

@@ -1193,50 +1193,73 @@ __global__ __launch_bounds__(256) void seed_kernel(PrefillArgs a, const int32_t 
 }
 
 // S_in(g + 1) = M_g S_in(g) + N_g for the middle segments g of one (sequence, head),
-// 16 state columns per workgroup, fp32
+// 16 state columns per workgroup, in fp32 (16x16x4 fp32 MFMAs: exact products,
+// fp32 sums). Wave w computes rows 16w .. 16w + 15 of the tile: lane (r, q) feeds
+// row 16w + r of M over the columns K/4 q .. K/4 (q + 1) - 1 as A operands, loaded
+// one step ahead, and the same rows of the tile (transposed in LDS) as B operands;
+// the accumulator starts from N_g. The steps are sequential, so the time per step
+// is one chain of K/4 MFMAs and one barrier.
 template <int K, int V>
-__global__ __launch_bounds__(256) void prefix_kernel(const int32_t *soff, int N, int H, SegBufs sb) {
-    __shared__ __attribute__((aligned(16))) float m[K][K + 4];
-    __shared__ float x[K][16];
-    constexpr int NV = V / 16, RPT = K / 16;
+__global__ __launch_bounds__(64 * K / 16) void prefix_kernel(const int32_t *soff, int N, int H, SegBufs sb) {
+    constexpr int NV = V / 16, KQ = K / 4, NT = 64 * K / 16;
+    __shared__ __attribute__((aligned(16))) float xt[2][16][K + 4];  // the tile, [buffer][column][row]
     const int b = blockIdx.x, vt = b % NV, nh = b / NV, n = nh / H, h = nh - (nh / H) * H;
     if (n >= N) return;
     const int s0 = soff[n], G = soff[n + 1] - s0;
     if (G < 3) return;
-    const int tid = threadIdx.x, col = tid & 15, rg = tid >> 4;
+    const int tid = threadIdx.x, l = tid & 63, r = l & 15, q = l >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const size_t kv = static_cast<size_t>(K) * V;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int row = rg * RPT + i;
-        x[row][col] = sb.sin[(static_cast<size_t>(s0 + 1) * H + h) * kv + static_cast<size_t>(row) * V + vt * 16 + col];
+    const int c0 = 16 * vt;
+    static_assert(NT == 4 * K, "one float4 of the K x 16 tile per thread");
+    {  // S_in(1): row tid / 4, columns 4 (tid % 4) .. + 3
+        const int row = tid >> 2, cq = 4 * (tid & 3);
+        const float4 v = *reinterpret_cast<const float4 *>(sb.sin + (static_cast<size_t>(s0 + 1) * H + h) * kv +
+                                                          static_cast<size_t>(row) * V + c0 + cq);
+        xt[0][cq][row] = v.x;
+        xt[0][cq + 1][row] = v.y;
+        xt[0][cq + 2][row] = v.z;
+        xt[0][cq + 3][row] = v.w;
     }
-    for (int gl = 1; gl <= G - 2; ++gl) {
-        const float *mg = sb.mapm + (static_cast<size_t>(s0 + gl) * H + h) * K * K;
-        const float *ng = sb.mapn + (static_cast<size_t>(s0 + gl) * H + h) * kv;
-        for (int p = tid; p < K * K / 4; p += 256) {
-            const int row = (4 * p) / K, c4 = (4 * p) % K;
-            *reinterpret_cast<float4 *>(&m[row][c4]) = reinterpret_cast<const float4 *>(mg)[p];
-        }
-        __syncthreads();
-        float y[RPT];
+    const int mrow = 16 * w + r;
+    // operands of step gl: M_gl row mrow, columns KQ q ..; N_gl rows 16w + 4q + e, column c0 + r
+    auto load_step = [&](float4 (&am)[KQ / 4], f4 &an, int gl) {
+        const float4 *mg = reinterpret_cast<const float4 *>(
+            sb.mapm + (static_cast<size_t>(s0 + gl) * H + h) * K * K + static_cast<size_t>(mrow) * K + KQ * q);
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) y[i] = ng[static_cast<size_t>(rg * RPT + i) * V + vt * 16 + col];
-        for (int kk = 0; kk < K; kk += 4) {
-            const float x0 = x[kk][col], x1 = x[kk + 1][col], x2 = x[kk + 2][col], x3 = x[kk + 3][col];
+        for (int j = 0; j < KQ / 4; ++j) am[j] = mg[j];
+        const float *ng = sb.mapn + (static_cast<size_t>(s0 + gl) * H + h) * kv + c0 + r;
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) {
-                const float4 mv = *reinterpret_cast<const float4 *>(&m[rg * RPT + i][kk]);
-                y[i] = fmaf(mv.x, x0, fmaf(mv.y, x1, fmaf(mv.z, x2, fmaf(mv.w, x3, y[i]))));
-            }
-        }
-        __syncthreads();
+        for (int e = 0; e < 4; ++e) an[e] = ng[static_cast<size_t>(16 * w + 4 * q + e) * V];
+    };
+    auto step = [&](const float4 (&am)[KQ / 4], f4 y, int gl, int cur) {
+        const float4 *xb = reinterpret_cast<const float4 *>(&xt[cur][r][KQ * q]);
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int row = rg * RPT + i;
-            x[row][col] = y[i];
-            sb.sin[(static_cast<size_t>(s0 + gl + 1) * H + h) * kv + static_cast<size_t>(row) * V + vt * 16 + col] = y[i];
+        for (int j = 0; j < KQ / 4; ++j) {
+            const float4 x = xb[j];
+            y = __builtin_amdgcn_mfma_f32_16x16x4f32(am[j].x, x.x, y, 0, 0, 0);
+            y = __builtin_amdgcn_mfma_f32_16x16x4f32(am[j].y, x.y, y, 0, 0, 0);
+            y = __builtin_amdgcn_mfma_f32_16x16x4f32(am[j].z, x.z, y, 0, 0, 0);
+            y = __builtin_amdgcn_mfma_f32_16x16x4f32(am[j].w, x.w, y, 0, 0, 0);
         }
+        // y[e] = S_in(gl + 1)[16w + 4q + e][c0 + r]
+        float *dst = sb.sin + (static_cast<size_t>(s0 + gl + 1) * H + h) * kv + c0 + r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[static_cast<size_t>(16 * w + 4 * q + e) * V] = y[e];
+        *reinterpret_cast<f4 *>(&xt[cur ^ 1][r][16 * w + 4 * q]) = y;
         __syncthreads();
+    };
+    // two register sets in turn: the loads of the next step overlap the current one
+    float4 m0[KQ / 4], m1[KQ / 4];
+    f4 n0, n1;
+    load_step(m0, n0, 1);
+    __syncthreads();
+    for (int gl = 1; gl <= G - 2; gl += 2) {
+        load_step(m1, n1, min(gl + 1, G - 2));
+        step(m0, n0, gl, 0);
+        if (gl + 1 > G - 2) break;
+        load_step(m0, n0, min(gl + 2, G - 2));
+        step(m1, n1, gl + 1, 1);
     }
 }
 
@@ -1399,7 +1422,7 @@ hipError_t launch_kv(const PrefillArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((seg_kernel<K, V>), dim3(static_cast<unsigned>(units)), dim3(64 * (K + V) / (16 * kSegNB)), 0,
                        st, a, off, soff, lay.L, recs, sb);
     if (maxc > 2 * static_cast<int64_t>(lay.L))
-        hipLaunchKernelGGL((prefix_kernel<K, V>), dim3(static_cast<unsigned>(a.N) * a.H * (V / 16)), dim3(256), 0, st,
+        hipLaunchKernelGGL((prefix_kernel<K, V>), dim3(static_cast<unsigned>(a.N) * a.H * (V / 16)), dim3(64 * K / 16), 0, st,
                            soff, a.N, a.H, sb);
     if ((e = launch_out<K, V>(a, off, soff, lay.L, recs, sb, units, side ? 1 : 2, st)) != hipSuccess) return e;
     if (side) e = hipStreamWaitEvent(st, side->join, 0);
