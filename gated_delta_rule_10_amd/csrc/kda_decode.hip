@@ -10,10 +10,13 @@
 // channel as in its section "KLA"; the state cache is one contiguous
 // [slots, H, d_k, d_v] array as in "线性注意力机制Kimi Linear架构解析与优化实践", section 3.2.
 //
-// Mapping: one 256-thread workgroup per (b, h). A state row of d_v floats is
-// covered by d_v/4 lanes reading float4, so one wave load instruction reads
-// 64 * 16 B = 1 KiB of consecutive rows (fully coalesced). Each lane keeps its
-// d_k*d_v/1024 float4s in registers between the read and the write. The small
+// Mapping: two 256-thread workgroups per (b, h), each with half of the d_v
+// columns: the column reductions run over d_k only, so the halves are
+// independent (they both read the small inputs). The RMS norm of the output
+// epilogue needs whole rows and keeps one workgroup per (b, h). A state row of
+// NC floats is covered by NC/4 lanes reading float4, so one wave load
+// instruction reads 64 * 16 B = 1 KiB in rows of NC * 4 bytes. Each lane keeps
+// its d_k*NC/1024 float4s in registers between the read and the write. The small
 // inputs are loaded first, so that they arrive while the state loads are in
 // flight: one load per key channel of the gate, k and q (staged through LDS as
 // (alpha, k, q) for the lanes of every row), and each lane's four columns of v,
@@ -27,10 +30,11 @@ namespace kda {
 namespace {
 
 constexpr int kDecWaves = 4;
+constexpr int kDecSplit = 2;  // workgroups per (b, h), each with d_v / kDecSplit columns
 
-template <int K, int V, typename TIn, typename TOut>
+template <int K, int V, int NC, typename TIn, typename TOut>
 __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
-    constexpr int LPR = V / 4;                       // lanes per state row
+    constexpr int LPR = NC / 4;                      // lanes per state row (NC of its d_v columns)
     constexpr int RPI = 64 / LPR;                    // rows per wave load
     constexpr int ITERS = K / (kDecWaves * RPI);     // float4 per lane
     static_assert(ITERS * kDecWaves * RPI == K, "row mapping must cover d_k");
@@ -42,7 +46,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int c4 = lane % LPR, rsub = lane / LPR;
-    const int bh = blockIdx.x;
+    const int bh = blockIdx.x / (V / NC), col0 = NC * (blockIdx.x - bh * (V / NC));
     const int b = bh / a.H, h = bh - b * a.H;
     // value head h reads key head h / (H / Hk)
     const size_t bhk = static_cast<size_t>(b) * a.Hk + h / (a.H / a.Hk);
@@ -55,11 +59,11 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
         kk = io<TIn>::load(static_cast<const TIn *>(a.k) + bhk * K + tid);
         qk = io<TIn>::load(static_cast<const TIn *>(a.q) + bhk * K + tid);
     }
-    const float4 vv = io<TIn>::load4(static_cast<const TIn *>(a.v) + static_cast<size_t>(bh) * V + c4 * 4);
+    const float4 vv = io<TIn>::load4(static_cast<const TIn *>(a.v) + static_cast<size_t>(bh) * V + col0 + c4 * 4);
     const float braw = a.by ? io<TIn>::load(static_cast<const TIn *>(a.by) + bh) : a.beta[bh];
     float4 zv = make_float4(1.f, 1.f, 1.f, 1.f), wv = zv;
-    if (a.z) zv = io<TIn>::load4(static_cast<const TIn *>(a.z) + static_cast<size_t>(bh) * V + c4 * 4);
-    if (a.norm && a.nw) wv = io<float>::load4(a.nw + c4 * 4);
+    if (a.z) zv = io<TIn>::load4(static_cast<const TIn *>(a.z) + static_cast<size_t>(bh) * V + col0 + c4 * 4);
+    if (a.norm && a.nw) wv = io<float>::load4(a.nw + col0 + c4 * 4);
 
     // ---- the state
     const int slot = a.slot_idx ? ld_meta(a.slot_idx, b) : b;
@@ -68,7 +72,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
         const int row = (it * kDecWaves + w) * RPI + rsub;
-        s[it] = io<float>::load4(S + row * V + c4 * 4);
+        s[it] = io<float>::load4(S + row * V + col0 + c4 * 4);
     }
 
     if (tid < K) {
@@ -115,7 +119,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
     const float bt = a.by ? sigmoid_f(braw) : braw;
     const float4 u = (vv - r) * bt;
     float4 ov = fma4(u, kq, p) * a.scale;
-    if (a.norm) {  // o / sqrt(mean o^2 + eps) over the LPR lanes of the row (uniform branch)
+    if (a.norm) {  // o / sqrt(mean o^2 + eps) over the LPR lanes of the row (uniform branch; NC == V)
         float ss = ov.x * ov.x + ov.y * ov.y + ov.z * ov.z + ov.w * ov.w;
 #pragma unroll
         for (int m = 1; m < LPR; m <<= 1) ss += __shfl_xor(ss, m);
@@ -128,26 +132,34 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
     }
     if (w == 0 && rsub == 0) {
         TOut *op = static_cast<TOut *>(a.o) + static_cast<size_t>(bh) * V;
-        io<TOut>::store4(op + c4 * 4, ov);
+        io<TOut>::store4(op + col0 + c4 * 4, ov);
     }
     // S = S' + k u^T
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
         const int row = (it * kDecWaves + w) * RPI + rsub;
-        io<float>::store4(S + row * V + c4 * 4, fma4(u, vec[row].y, s[it]));
+        io<float>::store4(S + row * V + col0 + c4 * 4, fma4(u, vec[row].y, s[it]));
     }
 }
 
+template <int K, int V, int NC>
+hipError_t launch_nc(const DecodeArgs &a, hipStream_t st) {
+    const dim3 grid(a.B * a.H * (V / NC)), block(64 * kDecWaves);
+    if (a.in_dtype == KDA_F32)
+        hipLaunchKernelGGL((decode_kernel<K, V, NC, float, float>), grid, block, 0, st, a);
+    else if (a.out_dtype == KDA_BF16)
+        hipLaunchKernelGGL((decode_kernel<K, V, NC, bf16_t, bf16_t>), grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL((decode_kernel<K, V, NC, bf16_t, float>), grid, block, 0, st, a);
+    return hipGetLastError();
+}
+
+// The RMS norm of the output epilogue spans a whole row of d_v columns, so it
+// keeps one workgroup per (b, h); otherwise kDecSplit workgroups share the columns.
 template <int K, int V>
 hipError_t launch_kv(const DecodeArgs &a, hipStream_t st) {
-    const dim3 grid(a.B * a.H), block(64 * kDecWaves);
-    if (a.in_dtype == KDA_F32)
-        hipLaunchKernelGGL((decode_kernel<K, V, float, float>), grid, block, 0, st, a);
-    else if (a.out_dtype == KDA_BF16)
-        hipLaunchKernelGGL((decode_kernel<K, V, bf16_t, bf16_t>), grid, block, 0, st, a);
-    else
-        hipLaunchKernelGGL((decode_kernel<K, V, bf16_t, float>), grid, block, 0, st, a);
-    return hipGetLastError();
+    if (a.norm || kDecSplit == 1) return launch_nc<K, V, V>(a, st);
+    return launch_nc<K, V, V / kDecSplit>(a, st);
 }
 
 }  // namespace
