@@ -1342,9 +1342,9 @@ struct WsLayout {
 // A second stream per device, with the events that fork it from and join it to
 // the caller's stream: the output pass of the segments 0 runs on it beside the
 // map pass, on the compute units the map pass leaves free (one workgroup per
-// middle segment and head). Created on first use, at default priority; calls
-// hold the lock while they enqueue, so the fork and join of concurrent callers
-// do not interleave. KDA_NO_SIDE_STREAM=1 keeps everything on the caller's stream.
+// middle segment and head). Created at the first prefill call on the device, at
+// default priority; calls hold the lock while they enqueue, so the fork and join
+// of concurrent callers do not interleave.
 struct SideStream {
     hipStream_t s = nullptr;
     hipEvent_t fork = nullptr, join = nullptr;
@@ -1353,12 +1353,8 @@ struct SideStream {
 std::mutex g_side_mu;
 SideStream *side_stream() {
     static SideStream per_dev[64];
-    static const bool off = [] {
-        const char *e = std::getenv("KDA_NO_SIDE_STREAM");
-        return e && std::atoi(e) != 0;
-    }();
     int dev = 0;
-    if (off || hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
     SideStream &ss = per_dev[dev];
     if (!ss.tried) {
         ss.tried = true;
@@ -1412,7 +1408,16 @@ hipError_t launch_kv(const PrefillArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((seed_kernel<K, V>), dim3(static_cast<unsigned>(a.N) * a.H), dim3(256), 0, st, a, soff, sb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    SideStream *side = side_stream();
+    // The second stream only pays when the output pass needs more than one round
+    // of workgroups (one per compute unit): then the segments 0 start early on
+    // the units the map pass leaves free. Every sequence has a segment and the
+    // segments hold at most L chunks each, which bounds their count from below
+    // (cu_seqlens stays on the device). KDA_SIDE_STREAM=0 or 1 (read at every
+    // call) turns it off or on regardless.
+    const size_t segs = std::max<size_t>(static_cast<size_t>(a.N), (static_cast<size_t>(maxc) + lay.L - 1) / lay.L);
+    bool use_side = segs * a.H > static_cast<size_t>(cu_count());
+    if (const char *e = std::getenv("KDA_SIDE_STREAM"); e && *e) use_side = std::atoi(e) != 0;
+    SideStream *side = use_side ? side_stream() : nullptr;
     if (side) {  // segments 0 of the output pass beside the map pass
         if ((e = hipEventRecord(side->fork, st)) != hipSuccess) return e;
         if ((e = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess) return e;
@@ -1440,6 +1445,7 @@ size_t prefill_mfma_workspace(int32_t N, int32_t T, int32_t H, int32_t K, int32_
 
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t st) {
     const std::lock_guard<std::mutex> lock(g_side_mu);  // one enqueue sequence at a time (shared side stream)
+    side_stream();  // created at the first call, used or not, so that a later captured call creates nothing
     if (a.K == 128 && a.V == 128) return launch_kv<128, 128>(a, st);
     if (a.K == 128 && a.V == 64) return launch_kv<128, 64>(a, st);
     if (a.K == 64 && a.V == 128) return launch_kv<64, 128>(a, st);

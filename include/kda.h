@@ -31,8 +31,12 @@
  *    call that needs it, default priority, kept until the process ends),
  *    forked from and joined back to `stream` with those events: the call as a
  *    whole is still ordered on `stream`, and can be captured in a HIP graph
- *    (the first call should then come before the capture). KDA_NO_SIDE_STREAM=1
- *    in the environment keeps all work on `stream`.
+ *    (the first prefill call on a device, which creates the stream, should
+ *    then come before the capture). By default the second stream is used when
+ *    the call has more state-pass segments than the device has compute units;
+ *    KDA_SIDE_STREAM=0 or 1 in the environment (read at every call) keeps all
+ *    work on `stream`, or uses the second stream whenever a sequence spans
+ *    several segments.
  *  - Every pointer must be 16-byte aligned; tensors are dense, row-major,
  *    with the layouts given below (last dimension contiguous).
  *  - Arguments are validated on the host before anything is enqueued. A

@@ -89,6 +89,7 @@ def test_output_epilogue(dt, norm, z_act):
 @pytest.mark.parametrize("seg", ["2", "16"])
 def test_state_slots(dt, seg, monkeypatch):
     monkeypatch.setenv("KDA_SEG_CHUNKS", seg)
+    monkeypatch.setenv("KDA_SIDE_STREAM", "1")
     # shuffled slots, a padding sequence and an empty one; several segments per sequence
     _prefill_case(24, [300, 0, 77, 260], 2, 2, 128, 128, dt, gates="plain", slots=[5, 2, -1, 0])
 
@@ -103,6 +104,7 @@ def test_no_tokens_with_slots_and_epilogue(dt):
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64), (64, 64)])
 def test_all_options_together(dk, dv, monkeypatch):
     monkeypatch.setenv("KDA_SEG_CHUNKS", "2")
+    monkeypatch.setenv("KDA_SIDE_STREAM", "1")
     _prefill_case(25, [333, 5, 180], 2, 4, dk, dv, "bf16", gates="pre", norm=True, z_act="sigmoid",
                   slots=[1, 3, 0])
 
@@ -195,12 +197,15 @@ def test_decode_steps_replayed_from_a_hip_graph_match_eager():
         _ = (state * 2).sum().item()   # eager work between replays
 
 
-def test_prefill_replayed_from_a_hip_graph_matches_eager(monkeypatch):
+@pytest.mark.parametrize("side", ["0", "1"])
+def test_prefill_replayed_from_a_hip_graph_matches_eager(side, monkeypatch):
     """Prefill (plain and extended, several segments per sequence, so every kernel
-    of the call runs) captured once in a HIP graph with caller-provided outputs and
+    of the call runs; with side = 1 the first segments on the library's second
+    stream) captured once in a HIP graph with caller-provided outputs and
     workspace, replayed three times with eager work and synchronisation between
     the replays: outputs and final states equal the eager ones bitwise."""
     monkeypatch.setenv("KDA_SEG_CHUNKS", "2")
+    monkeypatch.setenv("KDA_SIDE_STREAM", side)
     lens = [300, 77, 500]
     Hk, H, K, V = 2, 4, 128, 128
     T, N = sum(lens), len(lens)

@@ -98,10 +98,12 @@ def test_prefill_null_vs_zero_state_alias_and_determinism():
 
 @pytest.mark.parametrize("seg", ["1", "2", "3"])
 def test_prefill_segmented_state_pass(seg, monkeypatch):
-    """The state pass cut into segments of `seg` chunks (map pass, prefix over
-    segments, output pass) on ragged packed sequences, including empty ones,
-    with a random initial state; final_state aliasing initial_state."""
+    """The state pass cut into segments of `seg` chunks (map pass with the first
+    segments' output pass beside it on the second stream, prefix over segments,
+    output pass) on ragged packed sequences, including empty ones, with a random
+    initial state; final_state aliasing initial_state."""
     monkeypatch.setenv("KDA_SEG_CHUNKS", seg)
+    monkeypatch.setenv("KDA_SIDE_STREAM", "1")
     inp = inputs.prefill_inputs(11, [0, 700, 64, 1, 389, 0, 200], 3, 128, 128, "bf16", 0.1, "random")
     d = _prefill_case(inp)
     o1, s1 = gc.run_prefill(d)
@@ -115,6 +117,7 @@ def test_prefill_segmented_state_pass(seg, monkeypatch):
 @pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64), (64, 64)])
 def test_prefill_segmented_head_dims(dk, dv, monkeypatch):
     monkeypatch.setenv("KDA_SEG_CHUNKS", "2")
+    monkeypatch.setenv("KDA_SIDE_STREAM", "1")
     _prefill_case(inputs.prefill_inputs(12, [520, 70, 300], 2, dk, dv, "bf16", 0.1, "random"))
 
 

@@ -1,9 +1,9 @@
 """GPU parity on seeded random configurations through the C ABI: sequence count
 and lengths (empty, single-token, partial and several chunks), key-head
 grouping, head sizes, input type, gate form, output epilogue, slot caches and
-segment length (so that the map pass, the prefix and the output pass of the
-first segments on the second stream all take part), each against the fp64
-oracle with the same options."""
+segment length (so that the map pass, the prefix and the output pass all take
+part; odd cases run the first segments on the second stream), each against the
+fp64 oracle with the same options."""
 
 import numpy as np
 import pytest
@@ -43,6 +43,7 @@ def test_random_configuration(i, monkeypatch):
     print(f"  case {i}: {c}", flush=True)
     if c["seg"] is not None:
         monkeypatch.setenv("KDA_SEG_CHUNKS", c["seg"])
+    monkeypatch.setenv("KDA_SIDE_STREAM", str(i % 2))
     _prefill_case(2000 + i, c["lens"], c["Hk"], c["H"], c["K"], c["V"], c["dt"], gates=c["gates"], norm=c["norm"],
                   z_act=c["z_act"], slots=c["slots"])
 
