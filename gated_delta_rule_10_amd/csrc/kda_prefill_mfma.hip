@@ -33,10 +33,11 @@
 //    the fp16 range never limits the magnitude of v or of the state.
 //
 // Options of kda_chunk_fwd_ex: the gates from bf16 pre-activations are formed
-// in prep as the inputs are unpacked; grouped key heads only change which q/k
-// rows prep reads; slot-indexed states only change where the state passes read
-// the initial and write the final state; the RMS-norm / output-gate epilogue
-// runs in the output pass on an fp32 tile of each chunk's outputs.
+// in prep at the end of the item before the one that uses them (off the start
+// of an item, where every wave waits for them); grouped key heads only change
+// which q/k rows prep reads; slot-indexed states only change where the state
+// passes read the initial and write the final state; the RMS-norm / output-gate
+// epilogue runs in the output pass on an fp32 tile of each chunk's outputs.
 //
 // MFMA fragment conventions (v_mfma_f32_16x16x32_f16, lane l, r = l % 16,
 // g = l / 16): A operand holds A[r][k(g, e)], B operand B[k(g, e)][r], result
@@ -268,6 +269,25 @@ struct PrepRaw {
         if (!valid) return 0.f;
         return a.by ? sigmoid_f(__uint_as_float(betaw << 16)) : __uint_as_float(betaw);
     }
+    // With GX: the gate pre-activations as fp32 log alpha in gv, in the layout of
+    // fp32 gates (channels o .. o + 3, o + 4 .. o + 7). Called once the loads have
+    // landed, away from the start of the item that uses them.
+    __device__ __forceinline__ void activate(float gscale) {
+        if constexpr (GX) {
+#pragma unroll
+            for (int cb = 0; cb < K / 32; ++cb) {
+                const uint32_t w4[4] = {xv[cb].x, xv[cb].y, xv[cb].z, xv[cb].w};
+                float f[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    f[2 * e] = log_alpha_from(__uint_as_float(w4[e] << 16), gscale);
+                    f[2 * e + 1] = log_alpha_from(__uint_as_float(w4[e] & 0xFFFF0000u), gscale);
+                }
+                gv[cb][0] = make_float4(f[0], f[1], f[2], f[3]);
+                gv[cb][1] = make_float4(f[4], f[5], f[6], f[7]);
+            }
+        }
+    }
     // k, q and the inclusive scan of the log decay over the 16-token sub-chunk
     // (lanes r of a 16-lane row are its consecutive tokens), channels in chain order
     __device__ __forceinline__ void unpack(float (&kx)[K / 32][8], float (&qx)[K / 32][8], float (&sc)[K / 32][8],
@@ -280,17 +300,7 @@ struct PrepRaw {
             swap16(qq.x, qq.z);
             swap16(qq.y, qq.w);
             float gg[8];
-            if constexpr (GX) {
-                uint4 xx = xv[cb];
-                swap16(xx.x, xx.z);
-                swap16(xx.y, xx.w);
-                const uint32_t w4[4] = {xx.x, xx.y, xx.z, xx.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    gg[2 * e] = log_alpha_from(__uint_as_float(w4[e] << 16), gscale);
-                    gg[2 * e + 1] = log_alpha_from(__uint_as_float(w4[e] & 0xFFFF0000u), gscale);
-                }
-            } else {
+            {  // fp32 log alpha (with GX, as activate() left it)
                 float4 p = gv[cb][0], q4 = gv[cb][1];
                 swap16(p.x, q4.x);
                 swap16(p.y, q4.y);
@@ -349,6 +359,7 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
     PrepItem nx = prep_item(a, off, u < total ? u : 0);
     PrepRaw<K, GX> raw;
     raw.load(a, nx, u < total, tr, g);
+    raw.activate(a.gscale);
     for (; u < total; u += gridDim.x) {
     const PrepItem it = nx;
     const int c = it.c, h = it.h;
@@ -495,6 +506,7 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
         // (this item's inputs are read again: the registers now hold the next item's)
         PrepRaw<K, GX> cr;
         cr.load(a, it, true, tr, g);
+        cr.activate(a.gscale);
         cr.unpack(kx, qx, s, a.gscale);
         for (int ss = 0; ss < 16; ++ss) {
             float pa = 0.f, pp = 0.f;
@@ -574,6 +586,7 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
         }
     }
     if (tid < K) store_stream(reinterpret_cast<float *>(rec + R::GAM) + tid, sm.fac[15][tid]);
+    raw.activate(a.gscale);  // the next item's gates
     __syncthreads();  // the next item rewrites the LDS this one read last
     }
 }
