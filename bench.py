@@ -150,19 +150,33 @@ def cpu_baseline_prefill(d, target_s=12.0):
                        f"{elapsed:.2f} s", seconds=elapsed)
 
 
-def cpu_baseline_decode(d, steps=3):
+def cpu_baseline_decode(d, target_s=5.0):
+    """Time the fp64 oracle on the first decode steps of the same workload: one
+    step sets how many run in about target_s (at most the steps drawn)."""
     import numpy as np
     import oracle
     threads = _cpu_threads()
     state = d["state"].cpu().numpy().astype(np.float64)
-    host = {n: d[n][:steps].float().cpu().numpy() for n in ("q", "k", "v", "log_alpha", "beta")}
-    t0 = time.perf_counter()
-    for s in range(steps):
+    avail = d["q"].shape[0]
+
+    def step(s, host):
         oracle.decode(host["q"][s], host["k"][s], host["v"][s], host["log_alpha"][s],
                       host["beta"][s], state, nthreads=threads)
+
+    host = {n: d[n][:1].float().cpu().numpy() for n in ("q", "k", "v", "log_alpha", "beta")}
+    t0 = time.perf_counter()
+    step(0, host)
+    first = time.perf_counter() - t0
+    s0 = 1 if avail > 1 else 0  # the timed steps follow the untimed one when there are more
+    steps = int(max(1, min(avail - s0, target_s / max(first, 1e-4))))
+    host = {n: d[n][s0:s0 + steps].float().cpu().numpy() for n in ("q", "k", "v", "log_alpha", "beta")}
+    t0 = time.perf_counter()
+    for s in range(steps):
+        step(s, host)
     el = time.perf_counter() - t0
     return dict(value=el / steps * 1e6, unit="us/step", cores=threads, cpu=_cpu_model(), kind="oracle",
-                sample=f"fp64 oracle, {steps} decode steps of B=64, H=32, d=128")
+                sample=f"fp64 oracle, {steps} decode steps of B=64, H=32, d=128 (after one untimed step), "
+                       f"{el:.2f} s", seconds=el)
 
 
 def time_prefill_workload(name, steps, warmup, dev, stream):
