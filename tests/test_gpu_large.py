@@ -13,9 +13,14 @@ from tests import gpu_common as gc
 pytestmark = pytest.mark.gpu
 
 
-def test_prefill_beyond_2_31_elements():
+@pytest.mark.parametrize("seg", [None, "100"])
+def test_prefill_beyond_2_31_elements(seg, monkeypatch):
     """Two sequences (40,000 and 30,001 tokens), H = 256, d = 128, bf16: q holds
-    70,001 * 256 * 128 = 2.29e9 elements. Heads 0 and 255 against the oracle."""
+    70,001 * 256 * 128 = 2.29e9 elements. Heads 0 and 255 against the oracle.
+    With seg, segments of 100 chunks (map pass, prefix and the second stream)."""
+    if seg is not None:
+        monkeypatch.setenv("KDA_SEG_CHUNKS", seg)
+        monkeypatch.setenv("KDA_SIDE_STREAM", "1")
     d = inputs.device_prefill_inputs(71, [40000, 30001], 256, 128, 128, "bf16", 0.1, "random")
     assert d["q"].numel() > 2 ** 31
     o, sT = gc.run_prefill(d)
