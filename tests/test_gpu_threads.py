@@ -1,0 +1,76 @@
+"""Calls from several host threads at once, each on its own stream: the prefill's
+second stream and its fork/join events are shared per device, so the library
+enqueues one call's sequence at a time. Results equal one thread's, bit for bit.
+"""
+
+import threading
+
+import pytest
+import torch
+
+from gated_delta_rule_10_amd import inputs, kda
+from tests import gpu_common as gc
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("side", ["0", "1"])
+def test_prefill_and_decode_from_concurrent_threads(side, monkeypatch):
+    monkeypatch.setenv("KDA_SEG_CHUNKS", "2")
+    monkeypatch.setenv("KDA_SIDE_STREAM", side)
+    cases = [gc.to_device(inputs.prefill_inputs(80 + i, [300, 77, 500], 4, 128, 128, "bf16", 0.1, "random"))
+             for i in range(3)]
+    dec = inputs.device_decode_inputs(83, 4, 8, 4, 128, 128)
+    N, H, K, V = 3, 4, 128, 128
+
+    def buffers(d):
+        T = d["q"].shape[0]
+        return dict(o=torch.empty((T, H, V), dtype=torch.bfloat16, device="cuda"),
+                    fin=torch.empty((N, H, K, V), dtype=torch.float32, device="cuda"),
+                    ws=torch.empty(kda.kda_chunk_fwd_workspace_size(N, T, H, K, V, torch.bfloat16),
+                                   dtype=torch.uint8, device="cuda"))
+
+    def work(bufs, state, outs, stream):
+        for rep in range(3):
+            for d, b in zip(cases, bufs):
+                kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["cu_seqlens"],
+                                  initial_state=d["initial_state"], final_state=b["fin"], o=b["o"],
+                                  workspace=b["ws"], stream=stream)
+            for s in range(dec["q"].shape[0]):
+                kda.kda_decode_step(dec["q"][s], dec["k"][s], dec["v"][s], dec["log_alpha"][s], dec["beta"][s],
+                                    state, o=outs[s], stream=stream)
+
+    # one thread, for reference: the decode state after 3 x 4 steps from the same start
+    ref_bufs = [buffers(d) for d in cases]
+    ref_state = dec["state"].clone()
+    ref_outs = torch.empty((4, 8, H, V), dtype=torch.bfloat16, device="cuda")
+    work(ref_bufs, ref_state, ref_outs, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+
+    nthreads = 4
+    bufs = [[buffers(d) for d in cases] for _ in range(nthreads)]
+    states = [dec["state"].clone() for _ in range(nthreads)]
+    outs = [torch.empty((4, 8, H, V), dtype=torch.bfloat16, device="cuda") for _ in range(nthreads)]
+    streams = [torch.cuda.Stream() for _ in range(nthreads)]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    errors = []
+
+    def run(i):
+        try:
+            with torch.cuda.stream(streams[i]):
+                work(bufs[i], states[i], outs[i], streams[i])
+        except Exception as e:  # reported below, on the test's thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(nthreads)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(nthreads):
+        for b, r in zip(bufs[i], ref_bufs):
+            assert torch.equal(b["o"], r["o"]) and torch.equal(b["fin"], r["fin"]), f"thread {i}: prefill differs"
+        assert torch.equal(states[i], ref_state) and torch.equal(outs[i], ref_outs), f"thread {i}: decode differs"
