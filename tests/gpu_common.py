@@ -88,6 +88,44 @@ def err_over_rms(got, ref, bf16_rounded: bool = False) -> float:
     return float(d.max()) / max(rms, 1e-30)
 
 
+def norm_epilogue_bound(pre, tol, norm_eps, weight=None, gate=None):
+    """Per-element error bound of the RMS-norm epilogue's output, propagated from
+    the bar on the operator's own output o (every element of o within
+    e = tol * RMS(o)). With s = sqrt(mean over the row of o^2 + eps) and
+    y_i = w_i o_i / s, a change d in o moves y_i by
+    w_i (d_i / s - o_i (sum_j o_j d_j / d_v) / s^3), and |sum_j o_j d_j / d_v| <= e s,
+    so |dy_i| <= e |w_i| (1 / s + |o_i| / s^2); an output gate multiplies it by
+    |act(z_i)|. `pre` is the oracle's output before the epilogue, `gate` the
+    values act(z)."""
+    pre = np.asarray(pre, np.float64)
+    if pre.size == 0:
+        return pre
+    e = tol * float(np.sqrt(np.mean(pre * pre)))
+    s = np.sqrt(np.mean(pre * pre, axis=-1, keepdims=True) + norm_eps)
+    w = 1.0 if weight is None else np.abs(np.asarray(weight, np.float64))
+    bound = e * w * (1.0 / s + np.abs(pre) / (s * s))
+    if gate is not None:
+        bound = bound * np.abs(np.asarray(gate, np.float64))
+    return bound
+
+
+def assert_within_bound(name, got, ref, bound, bf16_rounded=False):
+    """Every element within its own bound (after half a bf16 ulp for bf16 outputs)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    if ref.size == 0:
+        return 0.0
+    d = np.abs(got - ref)
+    if bf16_rounded:
+        d = np.maximum(d - half_ulp_bf16(np.maximum(np.abs(ref), np.abs(got))), 0.0)
+    r = float(np.max(d / np.maximum(bound, 1e-300)))
+    print(f"  {name}: max error / propagated bound = {r:.3f} (err/RMS = {err_over_rms(got, ref, bf16_rounded):.3e})",
+          flush=True)
+    assert r <= 1.0, f"{name}: error {r:.3f} x its propagated bound"
+    return r
+
+
 def assert_close(name, got, ref, tol, bf16_rounded=False):
     e = err_over_rms(got, ref, bf16_rounded)
     print(f"  {name}: err/RMS = {e:.3e} (tol {tol:.0e})", flush=True)

@@ -54,6 +54,15 @@ def _prefill_case(seed, lens, Hk, H, K, V, dt, *, gates="pre", norm=False, z_act
         s0 = (0.02 * rng.standard_normal((N, H, K, V))).astype(np.float32)
         ref_o, ref_s = oo.prefill_ex(x["q"], x["k"], x["v"], cu, initial_state=s0, **kw_o)
     tol = gc.TOL_BF16 if bf else gc.TOL_F32
+    bound = None
+    if norm:  # the bar on the operator's o, carried through the row normalisation
+        kw_pre = {k: v for k, v in kw_o.items() if k not in ("norm", "norm_eps", "norm_weight", "out_gate",
+                                                              "out_gate_act")}
+        init = cache if slots is not None else s0
+        extra = dict(state_slots=s_np) if slots is not None else {}
+        pre, _ = oo.prefill_ex(x["q"], x["k"], x["v"], cu, initial_state=init, **extra, **kw_pre)
+        gate = None if z_act is None else oo.output_gate(np.ones_like(pre), x["out_gate"], z_act)
+        bound = gc.norm_epilogue_bound(pre, tol, 1e-5, x["norm_weight"], gate)
     for od in (out_dtypes or ([torch.bfloat16, torch.float32] if bf else [torch.float32])):
         if slots is not None:
             st = torch.from_numpy(cache).cuda()
@@ -64,7 +73,10 @@ def _prefill_case(seed, lens, Hk, H, K, V, dt, *, gates="pre", norm=False, z_act
             o, sT = kda.kda_chunk_fwd_ex(_t(x["q"], bf), _t(x["k"], bf), _t(x["v"], bf), torch.from_numpy(cu).cuda(),
                                          initial_state=torch.from_numpy(s0).cuda(), out_dtype=od, **kw_g)
         torch.cuda.synchronize()
-        gc.assert_close(f"o[{od}]", gc.host(o), ref_o, tol, bf16_rounded=od == torch.bfloat16)
+        if bound is None:
+            gc.assert_close(f"o[{od}]", gc.host(o), ref_o, tol, bf16_rounded=od == torch.bfloat16)
+        else:
+            gc.assert_within_bound(f"o[{od}]", gc.host(o), ref_o, bound, bf16_rounded=od == torch.bfloat16)
         gc.assert_close("final_state", gc.host(sT), ref_s, tol)
 
 
@@ -83,6 +95,21 @@ def test_gate_preactivations(dt):
 @pytest.mark.parametrize("norm,z_act", [(True, None), (False, "sigmoid"), (True, "none"), (True, "sigmoid")])
 def test_output_epilogue(dt, norm, z_act):
     _prefill_case(23, [190, 64, 1], 2, 2, 128, 128, dt, gates="plain", norm=norm, z_act=z_act)
+
+
+@pytest.mark.parametrize("case", [
+    dict(seed=7051, lens=[129, 129, 2, 128, 129, 127], Hk=3, H=6, K=64, V=128, z_act=None,
+         slots=[3, -1, 8, 5, 4, 6], seg="1", side="1"),
+    dict(seed=7114, lens=[1, 129], Hk=1, H=3, K=128, V=64, z_act="none", slots=[-1, 1], seg="3", side="0"),
+])
+def test_output_norm_strong_decay(case, monkeypatch):
+    """Strong decay (log alpha = -0.5 softplus(x)) and the RMS norm: rows whose
+    output is small before the norm (here down to 7 % of RMS(o)) are scaled up
+    by it, and their error with them, so o is held to the propagated bound."""
+    monkeypatch.setenv("KDA_SEG_CHUNKS", case["seg"])
+    monkeypatch.setenv("KDA_SIDE_STREAM", case["side"])
+    _prefill_case(case["seed"], case["lens"], case["Hk"], case["H"], case["K"], case["V"], "bf16", gates="pre",
+                  norm=True, z_act=case["z_act"], slots=case["slots"], decay=0.5)
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
