@@ -12,7 +12,7 @@ from tests.test_gpu_options import _prefill_case
 
 pytestmark = pytest.mark.gpu
 
-CASES = 24
+CASES = 64
 
 
 def _config(i):
@@ -46,6 +46,38 @@ def test_random_configuration(i, monkeypatch):
     monkeypatch.setenv("KDA_SIDE_STREAM", str(i % 2))
     _prefill_case(2000 + i, c["lens"], c["Hk"], c["H"], c["K"], c["V"], c["dt"], gates=c["gates"], norm=c["norm"],
                   z_act=c["z_act"], slots=c["slots"])
+
+
+def _large_config(i):
+    r = np.random.default_rng(95000 + i)
+    N = int(r.integers(1, 9))
+    lens = [int(np.exp(r.uniform(0, np.log(20000)))) if r.random() > 0.1 else 0 for _ in range(N)]
+    if sum(lens) == 0:
+        lens[0] = 5000
+    H = int(r.choice([4, 8, 16, 32]))
+    Hk = int(r.choice([d for d in (1, 2, 4) if H % d == 0]))
+    K, V = int(r.choice([64, 128])), int(r.choice([64, 128]))
+    gates = str(r.choice(["pre", "plain"]))
+    norm = bool(r.integers(0, 2))
+    z_act = [None, "none", "sigmoid"][int(r.integers(0, 3))]
+    slots = None
+    if r.integers(0, 2):
+        slots = [int(x) for x in r.permutation(N + 2)[:N]]
+    decay = float(r.choice([0.05, 0.1, 0.3]))
+    return dict(lens=lens, Hk=Hk, H=H, K=K, V=V, gates=gates, norm=norm, z_act=z_act, slots=slots, decay=decay)
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_large_configuration(i, monkeypatch):
+    """Up to 8 sequences of up to 20K tokens, H up to 32, bf16, with the library's
+    own segment length and choice of streams."""
+    import torch
+    monkeypatch.delenv("KDA_SEG_CHUNKS", raising=False)
+    monkeypatch.delenv("KDA_SIDE_STREAM", raising=False)
+    c = _large_config(i)
+    print(f"  large case {i}: T={sum(c['lens'])} {c}", flush=True)
+    _prefill_case(8000 + i, c["lens"], c["Hk"], c["H"], c["K"], c["V"], "bf16", gates=c["gates"], norm=c["norm"],
+                  z_act=c["z_act"], slots=c["slots"], decay=c["decay"], out_dtypes=[torch.bfloat16])
 
 
 def _decode_config(i):
