@@ -324,10 +324,11 @@ def pin_contraction_bound(oracle):
         prev = cur
 
 
-def load_worked_example(name="worked_3tok_dk2.json"):
+def load_worked_example(name="worked_3tok_dk2.json", scaled=False):
     """A hand-derived example under tests/golden/ (exact fractions), as arrays:
     q, k, v, log_alpha [T, 1, dim], beta [T, 1], initial state [1, 1, K, V],
-    expected o [T, 1, V] and final state [1, 1, K, V]."""
+    expected o [T, 1, V] and final state [1, 1, K, V]; with `scaled`, also the
+    read-out scale and the expected o at that scale (appended)."""
     import json
     import os
     from fractions import Fraction
@@ -341,21 +342,27 @@ def load_worked_example(name="worked_3tok_dk2.json"):
     s0 = np.array([[num(x) for x in row] for row in ex["initial_state"]])[None, None]
     o = np.array([[num(x) for x in row] for row in ex["expected"]["o"]])[:, None, :]
     sT = np.array([[num(x) for x in row] for row in ex["expected"]["final_state"]])[None, None]
-    return arr("q"), arr("k"), arr("v"), np.log(arr("alpha")), beta, s0, o, sT
+    out = (arr("q"), arr("k"), arr("v"), np.log(arr("alpha")), beta, s0, o, sT)
+    if scaled:
+        o_s = np.array([[num(x) for x in row] for row in ex["scaled"]["o"]])[:, None, :]
+        out = out + (num(ex["scaled"]["scale"]), o_s)
+    return out
 
 
 def pin_worked_example(oracle):
-    """Prefill and decode reproduce the hand-derived worked example (the gates
-    reach the oracle as fp32 log alpha: compared to a few fp32 ulps)."""
-    q, k, v, g, b, s0, o_ref, s_ref = load_worked_example()
+    """Prefill and decode reproduce the hand-derived worked example, at scale 1
+    and at its read-out scale 1/2 (the gates reach the oracle as fp32 log alpha:
+    compared to a few fp32 ulps)."""
+    q, k, v, g, b, s0, o_ref, s_ref, sc, o_sc = load_worked_example(scaled=True)
     T = q.shape[0]
-    o, sT = oracle.prefill(q, k, v, g, b, [0, T], 1.0, s0)
-    assert np.abs(o - o_ref).max() < 1e-6 and np.abs(sT - s_ref).max() < 1e-6
-    state = np.ascontiguousarray(s0[0][None], dtype=np.float64)
-    for t in range(T):
-        od = oracle.decode(q[t:t + 1], k[t:t + 1], v[t:t + 1], g[t:t + 1], b[t:t + 1], state)
-        assert np.abs(od[0] - o_ref[t]).max() < 1e-6
-    assert np.abs(state - s_ref).max() < 1e-6
+    for scale, o_exp in ((1.0, o_ref), (sc, o_sc)):
+        o, sT = oracle.prefill(q, k, v, g, b, [0, T], scale, s0)
+        assert np.abs(o - o_exp).max() < 1e-6 and np.abs(sT - s_ref).max() < 1e-6
+        state = np.array(s0[0][None], dtype=np.float64)  # a copy: decode updates it in place
+        for t in range(T):
+            od = oracle.decode(q[t:t + 1], k[t:t + 1], v[t:t + 1], g[t:t + 1], b[t:t + 1], state, scale=scale)
+            assert np.abs(od[0] - o_exp[t]).max() < 1e-6
+        assert np.abs(state - s_ref).max() < 1e-6
 
 
 ALL_PINS = [

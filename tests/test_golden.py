@@ -1,6 +1,6 @@
 """The oracle against the hand-derived worked example under tests/golden/
 (exact fractions; the fixture cites the passages it follows and shows its
-derivation), and how many of the oracle mutants that example catches by itself."""
+derivation), and that this example catches every oracle mutant by itself."""
 
 import shutil
 import subprocess
@@ -16,9 +16,9 @@ def test_oracle_reproduces_the_worked_example():
 
 
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
-def test_the_worked_example_alone_catches_most_mutants(tmp_path):
-    """Every mutant of the recurrence's arithmetic except the output scale (the
-    example runs at scale 1) changes the example's numbers."""
+def test_the_worked_example_alone_catches_every_mutant(tmp_path):
+    """Every mutant of the recurrence's arithmetic, the output scale included (the
+    example also runs at scale 1/2), changes the example's numbers."""
     import os
     from tests.test_oracle import MUTANTS
     src = open(os.path.join(os.path.dirname(oracle.__file__), "kda_oracle.c")).read()
@@ -33,4 +33,4 @@ def test_the_worked_example_alone_catches_most_mutants(tmp_path):
             missed.append(name)
         except AssertionError:
             pass
-    assert missed == ["no_scale"], missed
+    assert missed == [], missed
