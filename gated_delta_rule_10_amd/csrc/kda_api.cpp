@@ -160,9 +160,9 @@ const char *kda_status_string(kda_status_t s) {
 size_t kda_chunk_fwd_workspace_size(int32_t N, int32_t T_total, int32_t H, int32_t d_k,
                                     int32_t d_v, kda_dtype_t in_dtype) {
     if (N < 1 || H < 1 || T_total < 0 || !head_dim_ok(d_k) || !head_dim_ok(d_v)) return 0;
-    // the bf16 path stages every chunk's state-independent operands in the workspace
+    // both paths stage every chunk's state-independent operands in the workspace
     if (in_dtype == KDA_BF16 && !force_valu()) return kda::prefill_mfma_workspace(N, T_total, H, d_k, d_v);
-    return 0;
+    return kda::prefill_valu_workspace(N, T_total, H, d_k);
 }
 
 

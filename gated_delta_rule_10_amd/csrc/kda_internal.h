@@ -21,7 +21,7 @@ struct PrefillArgs {
     int32_t N, T, H, K, V;
     float scale;
     kda_dtype_t in_dtype, out_dtype;
-    void *ws;                    // caller workspace (matrix-core path)
+    void *ws;                    // caller workspace (the per-chunk records)
     size_t ws_bytes;
     // options (kda_options_t); neutral values give the plain operator
     int32_t Hk;                  // key/query heads; value head h uses key head h / (H / Hk)
@@ -67,5 +67,7 @@ hipError_t launch_epilogue(const PrefillArgs &a, hipStream_t stream);
 
 // Workspace bytes of the matrix-core prefill (0 for d_k/d_v it cannot run).
 size_t prefill_mfma_workspace(int32_t N, int32_t T, int32_t H, int32_t K, int32_t V);
+// workspace of the fp32 vector-ALU path: one fp32 record per (chunk slot, head)
+size_t prefill_valu_workspace(int32_t N, int32_t T, int32_t H, int32_t K);
 
 }  // namespace kda

@@ -1,4 +1,4 @@
-// KDA chunk prefill, fp32 vector-ALU kernel (the fp32-input path).
+// KDA chunk prefill, fp32 vector-ALU kernels (the fp32-input path).
 //
 // Chunkwise form ("Kimi Linear爆发背后的秘密" page, section "硬件效率的深度优化":
 // parallel inside a chunk, recurrent across chunks, WY representation, UT
@@ -20,9 +20,19 @@
 // Rows past the end of a partial chunk are zero-filled with g = 0 and
 // beta = 0, which makes them contribute nothing.
 //
-// Mapping: one 256-thread workgroup per (sequence, head, 16 value columns);
-// the chunk's q/k/G tiles, A/T, P, the 16-column state slice and the
-// pseudo-values live in LDS (about 149 KB at d_k = 128).
+// Two kernels:
+//  * valu_prep_kernel, one 256-thread workgroup per (chunk, head), all in
+//    parallel: everything that does not depend on the state (the cumulative
+//    decay, A, P, T = (I + A)^{-1}, the decayed operands) into an fp32 record
+//    in the workspace;
+//  * valu_state_kernel, one 256-thread workgroup per (sequence, head, 16 value
+//    columns), sequential over the chunks of the sequence: the state-dependent
+//    products, with the chunk's record, the state slice and the pseudo-values
+//    in LDS (about 149 KB at d_k = 128).
+// Record slots: chunk c of sequence n has id floor(cu[n] / 64) + n + c. The ids
+// increase with n and c and stay distinct (floor(a/64) + ceil(b/64) <=
+// floor((a + b)/64) + 1), and they stay below ceil(T/64) + N; an empty
+// sequence leaves one id unused.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -30,30 +40,160 @@ namespace kda {
 namespace {
 
 constexpr int kC = 64;    // chunk length
-constexpr int kVT = 16;   // value columns per workgroup
+constexpr int kVT = 16;   // value columns per workgroup of the state pass
 constexpr int kNT = 256;  // threads per workgroup
 
+// fp32 record of one (chunk, head), row-major, each part 256-B aligned
 template <int K>
-struct ValuSmem {
+struct ValuRec {
+    static constexpr size_t TB = 0;                    // [64][64] T Diag(beta), zero above the diagonal
+    static constexpr size_t P = TB + kC * kC * 4;      // [64][64] P, zero above the diagonal
+    static constexpr size_t KE = P + kC * kC * 4;      // [64][K] K . e^G
+    static constexpr size_t QE = KE + kC * K * 4;      // [64][K] Q . e^G
+    static constexpr size_t KG = QE + kC * K * 4;      // [64][K] K . e^{G_n - G}
+    static constexpr size_t GAM = KG + kC * K * 4;     // [K] e^{G_n}
+    static constexpr size_t BYTES = (GAM + K * 4 + 255) / 256 * 256;
+};
+
+// record slots per head: an upper bound of the chunk ids
+inline size_t valu_slots(int32_t T, int32_t N) { return static_cast<size_t>((T + kC - 1) / kC) + N; }
+
+__device__ __forceinline__ int valu_base(const int32_t *cu, int n) { return cu[n] / kC + n; }
+
+// record id -> (sequence n, chunk c inside it); false for an unused id
+__device__ __forceinline__ bool valu_item(const int32_t *cu, int N, int id, int &n, int &c) {
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (valu_base(cu, mid) <= id) lo = mid; else hi = mid - 1;
+    }
+    n = lo;
+    c = id - valu_base(cu, lo);
+    return c >= 0 && c < (cu[lo + 1] - cu[lo] + kC - 1) / kC;
+}
+
+template <int K>
+struct PrepSm {
     static constexpr int KP = K + 1, CP = kC + 1;
-    float G[kC * KP];   // cumulative log decay, then K . e^{G_n - G}
-    float KK[kC * KP];  // k, then K . e^G
-    float QQ[kC * KP];  // q, then Q . e^G
+    float G[kC * KP];   // cumulative log decay
+    float KK[kC * KP];  // k
+    float QQ[kC * KP];  // q
     float A[kC * CP];   // strict-lower A, then T = (I + A)^{-1} below the diagonal
     float P[kC * CP];
-    float S[K * kVT];
-    float X[kC * kVT];  // v, then Diag(beta)(V - (K.e^G) S)
-    float U[kC * kVT];  // U'
     float glast[K];
-    float gam[K];
     float bet[kC];
 };
 
+template <int K, typename TIn>
+__global__ __launch_bounds__(kNT) void valu_prep_kernel(PrefillArgs a, char *recs, int nslot) {
+    constexpr int KP = K + 1, CP = kC + 1;
+    using R = ValuRec<K>;
+    __shared__ PrepSm<K> sm;
+    const int tid = threadIdx.x;
+    const int H = a.H, id = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+    int n, c;
+    if (!valu_item(a.cu_seqlens, a.N, id, n, c)) return;
+    const int t0 = a.cu_seqlens[n] + c * kC, nt = min(kC, a.cu_seqlens[n + 1] - t0);
+    const TIn *qg = static_cast<const TIn *>(a.q);
+    const TIn *kg = static_cast<const TIn *>(a.k);
+    const int Hk = a.Hk, hk = h / (H / Hk);  // key head of value head h
+    for (int idx = tid; idx < kC * K; idx += kNT) {
+        const int r = idx / K, i = idx % K;
+        const bool ok = r < nt;
+        const size_t off = (static_cast<size_t>(t0 + r) * H + h) * K + i;
+        const size_t offk = (static_cast<size_t>(t0 + r) * Hk + hk) * K + i;
+        sm.KK[r * KP + i] = ok ? io<TIn>::load(kg + offk) : 0.f;
+        sm.QQ[r * KP + i] = ok ? io<TIn>::load(qg + offk) : 0.f;
+        float gv = 0.f;
+        if (ok) gv = a.gx ? log_alpha_from(io<TIn>::load(static_cast<const TIn *>(a.gx) + off), a.gscale) : a.g[off];
+        sm.G[r * KP + i] = gv;
+    }
+    if (tid < kC) {
+        float bv = 0.f;
+        if (tid < nt) {
+            const size_t off = static_cast<size_t>(t0 + tid) * H + h;
+            bv = a.by ? sigmoid_f(io<TIn>::load(static_cast<const TIn *>(a.by) + off)) : a.beta[off];
+        }
+        sm.bet[tid] = bv;
+    }
+    __syncthreads();
+    if (tid < K) {  // inclusive cumulative sum of log alpha over the chunk
+        float acc = 0.f;
+        for (int r = 0; r < kC; ++r) {
+            acc += sm.G[r * KP + tid];
+            sm.G[r * KP + tid] = acc;
+        }
+        sm.glast[tid] = acc;
+    }
+    __syncthreads();
+    for (int p = tid; p < kC * kC; p += kNT) {  // A and P, one (r, s) pair each
+        const int r = p / kC, s = p % kC;
+        float aa = 0.f, pp = 0.f;
+        if (s <= r) {
+            for (int i = 0; i < K; ++i) {
+                const float ks = sm.KK[s * KP + i] * __expf(sm.G[r * KP + i] - sm.G[s * KP + i]);
+                aa = fmaf(sm.KK[r * KP + i], ks, aa);
+                pp = fmaf(sm.QQ[r * KP + i], ks, pp);
+            }
+        }
+        sm.A[r * CP + s] = s < r ? sm.bet[r] * aa : 0.f;
+        sm.P[r * CP + s] = pp;
+    }
+    __syncthreads();
+    // T = (I + A)^{-1}, row by row: T[r][c] = -sum_{c<=s<r} A[r][s] T[s][c],
+    // T[c][c] = 1. Row r of T overwrites row r of A once it is complete.
+    for (int r = 1; r < kC; ++r) {
+        float t = 0.f;
+        if (tid < r) {
+            t = -sm.A[r * CP + tid];
+            for (int s = tid + 1; s < r; ++s) t = fmaf(-sm.A[r * CP + s], sm.A[s * CP + tid], t);
+        }
+        __syncthreads();
+        if (tid < r) sm.A[r * CP + tid] = t;
+        __syncthreads();
+    }
+    char *rec = recs + (static_cast<size_t>(h) * nslot + id) * R::BYTES;
+    float *tb = reinterpret_cast<float *>(rec + R::TB), *pm = reinterpret_cast<float *>(rec + R::P);
+    for (int p = tid; p < kC * kC; p += kNT) {
+        const int r = p / kC, s = p % kC;
+        const float t = s < r ? sm.A[r * CP + s] : (s == r ? 1.f : 0.f);
+        tb[p] = t * sm.bet[s];
+        pm[p] = sm.P[r * CP + s];
+    }
+    float *ke = reinterpret_cast<float *>(rec + R::KE), *qe = reinterpret_cast<float *>(rec + R::QE);
+    float *kgn = reinterpret_cast<float *>(rec + R::KG);
+    for (int idx = tid; idx < kC * K; idx += kNT) {
+        const int r = idx / K, i = idx % K;
+        const float G = sm.G[r * KP + i];
+        const float e1 = __expf(G), e2 = __expf(sm.glast[i] - G);
+        const float kv = sm.KK[r * KP + i];
+        ke[idx] = kv * e1;
+        qe[idx] = sm.QQ[r * KP + i] * e1;
+        kgn[idx] = kv * e2;
+    }
+    if (tid < K) reinterpret_cast<float *>(rec + R::GAM)[tid] = __expf(sm.glast[tid]);
+}
+
+template <int K>
+struct StateSm {
+    static constexpr int KP = K + 1, CP = kC + 1;
+    float KE[kC * KP];  // K . e^G
+    float QE[kC * KP];  // Q . e^G
+    float KG[kC * KP];  // K . e^{G_n - G}
+    float TB[kC * CP];  // T Diag(beta)
+    float P[kC * CP];
+    float S[K * kVT];
+    float X[kC * kVT];  // v, then V - (K.e^G) S
+    float U[kC * kVT];  // U'
+    float gam[K];
+};
+
 template <int K, int V, typename TIn, typename TOut>
-__global__ __launch_bounds__(kNT) void prefill_valu_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kNT) void valu_state_kernel(PrefillArgs a, const char *recs, int nslot) {
     constexpr int KP = K + 1, CP = kC + 1;
     constexpr int NVT = V / kVT;
-    __shared__ ValuSmem<K> sm;
+    using R = ValuRec<K>;
+    __shared__ StateSm<K> sm;
     const int tid = threadIdx.x;
     int bid = blockIdx.x;
     const int vt = bid % NVT;
@@ -62,8 +202,6 @@ __global__ __launch_bounds__(kNT) void prefill_valu_kernel(PrefillArgs a) {
     const int j0 = vt * kVT;
     const int H = a.H;
     const int tbeg = a.cu_seqlens[n], tend = a.cu_seqlens[n + 1];
-    const TIn *qg = static_cast<const TIn *>(a.q);
-    const TIn *kg = static_cast<const TIn *>(a.k);
     const TIn *vg = static_cast<const TIn *>(a.v);
     TOut *og = static_cast<TOut *>(a.o);
     // states: [N, H, K, V], or with slots a cache [slots, H, K, V] read and written at slot[n]
@@ -72,118 +210,74 @@ __global__ __launch_bounds__(kNT) void prefill_valu_kernel(PrefillArgs a) {
     const size_t sbase = (static_cast<size_t>(slot) * H + h) * static_cast<size_t>(K) * V;
     const float *s0 = slot >= 0 ? a.s0 : nullptr;
     float *sT = slot >= 0 ? a.sT : nullptr;
-    const int Hk = a.Hk, hk = h / (H / Hk);  // key head of value head h
+    const char *hrec = recs + static_cast<size_t>(h) * nslot * R::BYTES;
+    const int base = valu_base(a.cu_seqlens, n);
 
     for (int idx = tid; idx < K * kVT; idx += kNT) {
         const int i = idx / kVT, c = idx % kVT;
         sm.S[idx] = s0 ? s0[sbase + static_cast<size_t>(i) * V + j0 + c] : 0.f;
     }
 
-    for (int t0 = tbeg; t0 < tend; t0 += kC) {
+    for (int t0 = tbeg, c = 0; t0 < tend; t0 += kC, ++c) {
         const int nt = min(kC, tend - t0);
+        const char *rec = hrec + static_cast<size_t>(base + c) * R::BYTES;
         __syncthreads();
-        for (int idx = tid; idx < kC * K; idx += kNT) {
-            const int r = idx / K, i = idx % K;
-            const bool ok = r < nt;
-            const size_t off = (static_cast<size_t>(t0 + r) * H + h) * K + i;
-            const size_t offk = (static_cast<size_t>(t0 + r) * Hk + hk) * K + i;
-            sm.KK[r * KP + i] = ok ? io<TIn>::load(kg + offk) : 0.f;
-            sm.QQ[r * KP + i] = ok ? io<TIn>::load(qg + offk) : 0.f;
-            float gv = 0.f;
-            if (ok) gv = a.gx ? log_alpha_from(io<TIn>::load(static_cast<const TIn *>(a.gx) + off), a.gscale) : a.g[off];
-            sm.G[r * KP + i] = gv;
+        {
+            const float *tb = reinterpret_cast<const float *>(rec + R::TB);
+            const float *pm = reinterpret_cast<const float *>(rec + R::P);
+            for (int p = tid; p < kC * kC; p += kNT) {
+                const int r = p / kC, s = p % kC;
+                sm.TB[r * CP + s] = tb[p];
+                sm.P[r * CP + s] = pm[p];
+            }
+            const float *ke = reinterpret_cast<const float *>(rec + R::KE);
+            const float *qe = reinterpret_cast<const float *>(rec + R::QE);
+            const float *kgn = reinterpret_cast<const float *>(rec + R::KG);
+            for (int idx = tid; idx < kC * K; idx += kNT) {
+                const int r = idx / K, i = idx % K;
+                sm.KE[r * KP + i] = ke[idx];
+                sm.QE[r * KP + i] = qe[idx];
+                sm.KG[r * KP + i] = kgn[idx];
+            }
+            if (tid < K) sm.gam[tid] = reinterpret_cast<const float *>(rec + R::GAM)[tid];
         }
         for (int idx = tid; idx < kC * kVT; idx += kNT) {
-            const int r = idx / kVT, c = idx % kVT;
-            sm.X[idx] = r < nt ? io<TIn>::load(vg + (static_cast<size_t>(t0 + r) * H + h) * V + j0 + c)
-                               : 0.f;
-        }
-        if (tid < kC) {
-            float bv = 0.f;
-            if (tid < nt) {
-                const size_t off = static_cast<size_t>(t0 + tid) * H + h;
-                bv = a.by ? sigmoid_f(io<TIn>::load(static_cast<const TIn *>(a.by) + off)) : a.beta[off];
-            }
-            sm.bet[tid] = bv;
+            const int r = idx / kVT, cc = idx % kVT;
+            sm.X[idx] = r < nt ? io<TIn>::load(vg + (static_cast<size_t>(t0 + r) * H + h) * V + j0 + cc) : 0.f;
         }
         __syncthreads();
-        if (tid < K) {  // inclusive cumulative sum of log alpha over the chunk
+        for (int idx = tid; idx < kC * kVT; idx += kNT) {  // X = V - (K.e^G) S
+            const int r = idx / kVT, cc = idx % kVT;
             float acc = 0.f;
-            for (int r = 0; r < kC; ++r) {
-                acc += sm.G[r * KP + tid];
-                sm.G[r * KP + tid] = acc;
-            }
-            sm.glast[tid] = acc;
-            sm.gam[tid] = __expf(acc);
+            for (int i = 0; i < K; ++i) acc = fmaf(sm.KE[r * KP + i], sm.S[i * kVT + cc], acc);
+            sm.X[idx] -= acc;
         }
         __syncthreads();
-        for (int p = tid; p < kC * kC; p += kNT) {  // A and P, one (r, s) pair each
-            const int r = p / kC, s = p % kC;
-            float aa = 0.f, pp = 0.f;
-            if (s <= r) {
-                for (int i = 0; i < K; ++i) {
-                    const float ks = sm.KK[s * KP + i] * __expf(sm.G[r * KP + i] - sm.G[s * KP + i]);
-                    aa = fmaf(sm.KK[r * KP + i], ks, aa);
-                    pp = fmaf(sm.QQ[r * KP + i], ks, pp);
-                }
-            }
-            sm.A[r * CP + s] = s < r ? sm.bet[r] * aa : 0.f;
-            sm.P[r * CP + s] = pp;
-        }
-        __syncthreads();
-        // T = (I + A)^{-1}, row by row: T[r][c] = -sum_{c<=s<r} A[r][s] T[s][c],
-        // T[c][c] = 1. Row r of T overwrites row r of A once it is complete.
-        for (int r = 1; r < kC; ++r) {
-            float t = 0.f;
-            if (tid < r) {
-                t = -sm.A[r * CP + tid];
-                for (int s = tid + 1; s < r; ++s) t = fmaf(-sm.A[r * CP + s], sm.A[s * CP + tid], t);
-            }
-            __syncthreads();
-            if (tid < r) sm.A[r * CP + tid] = t;
-            __syncthreads();
-        }
-        for (int idx = tid; idx < kC * K; idx += kNT) {  // decayed operands, in place
-            const int r = idx / K, i = idx % K;
-            const float G = sm.G[r * KP + i];
-            const float e1 = __expf(G), e2 = __expf(sm.glast[i] - G);
-            const float kv = sm.KK[r * KP + i];
-            sm.KK[r * KP + i] = kv * e1;
-            sm.QQ[r * KP + i] *= e1;
-            sm.G[r * KP + i] = kv * e2;
-        }
-        __syncthreads();
-        for (int idx = tid; idx < kC * kVT; idx += kNT) {  // X = Diag(beta)(V - (K.e^G) S)
-            const int r = idx / kVT, c = idx % kVT;
+        for (int idx = tid; idx < kC * kVT; idx += kNT) {  // U' = T Diag(beta) X
+            const int r = idx / kVT, cc = idx % kVT;
             float acc = 0.f;
-            for (int i = 0; i < K; ++i) acc = fmaf(sm.KK[r * KP + i], sm.S[i * kVT + c], acc);
-            sm.X[idx] = sm.bet[r] * (sm.X[idx] - acc);
-        }
-        __syncthreads();
-        for (int idx = tid; idx < kC * kVT; idx += kNT) {  // U' = T X
-            const int r = idx / kVT, c = idx % kVT;
-            float acc = sm.X[idx];
-            for (int s = 0; s < r; ++s) acc = fmaf(sm.A[r * CP + s], sm.X[s * kVT + c], acc);
+            for (int s = 0; s <= r; ++s) acc = fmaf(sm.TB[r * CP + s], sm.X[s * kVT + cc], acc);
             sm.U[idx] = acc;
         }
         __syncthreads();
         for (int idx = tid; idx < kC * kVT; idx += kNT) {  // O = (Q.e^G) S + P U'
-            const int r = idx / kVT, c = idx % kVT;
+            const int r = idx / kVT, cc = idx % kVT;
             if (r < nt) {
                 float acc = 0.f;
-                for (int i = 0; i < K; ++i) acc = fmaf(sm.QQ[r * KP + i], sm.S[i * kVT + c], acc);
-                for (int s = 0; s <= r; ++s) acc = fmaf(sm.P[r * CP + s], sm.U[s * kVT + c], acc);
-                io<TOut>::store(og + (static_cast<size_t>(t0 + r) * H + h) * V + j0 + c, a.scale * acc);
+                for (int i = 0; i < K; ++i) acc = fmaf(sm.QE[r * KP + i], sm.S[i * kVT + cc], acc);
+                for (int s = 0; s <= r; ++s) acc = fmaf(sm.P[r * CP + s], sm.U[s * kVT + cc], acc);
+                io<TOut>::store(og + (static_cast<size_t>(t0 + r) * H + h) * V + j0 + cc, a.scale * acc);
             }
         }
         __syncthreads();
         for (int idx = tid; idx < K * kVT; idx += kNT) {  // S <- e^{G_n} S + (K.e^{G_n-G})^T U'
-            const int i = idx / kVT, c = idx % kVT;
+            const int i = idx / kVT, cc = idx % kVT;
             float acc = sm.gam[i] * sm.S[idx];
-            for (int r = 0; r < kC; ++r) acc = fmaf(sm.G[r * KP + i], sm.U[r * kVT + c], acc);
+            for (int r = 0; r < kC; ++r) acc = fmaf(sm.KG[r * KP + i], sm.U[r * kVT + cc], acc);
             sm.S[idx] = acc;
         }
     }
+    __syncthreads();
     if (sT) {
         for (int idx = tid; idx < K * kVT; idx += kNT) {
             const int i = idx / kVT, c = idx % kVT;
@@ -237,13 +331,22 @@ hipError_t launch_epi(const PrefillArgs &a, hipStream_t st) {
 
 template <int K, int V>
 hipError_t launch_kv(const PrefillArgs &a, hipStream_t st) {
-    const dim3 grid(a.N * a.H * (V / kVT)), block(kNT);
+    const int nslot = static_cast<int>(valu_slots(a.T, a.N));
+    char *recs = static_cast<char *>(a.ws);
+    if (a.T > 0) {
+        const dim3 pg(static_cast<unsigned>(nslot) * a.H), pb(kNT);
+        if (a.in_dtype == KDA_F32) hipLaunchKernelGGL((valu_prep_kernel<K, float>), pg, pb, 0, st, a, recs, nslot);
+        else hipLaunchKernelGGL((valu_prep_kernel<K, bf16_t>), pg, pb, 0, st, a, recs, nslot);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const dim3 grid(static_cast<unsigned>(a.N) * a.H * (V / kVT)), block(kNT);
     if (a.in_dtype == KDA_F32)
-        hipLaunchKernelGGL((prefill_valu_kernel<K, V, float, float>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((valu_state_kernel<K, V, float, float>), grid, block, 0, st, a, recs, nslot);
     else if (a.out_dtype == KDA_BF16)
-        hipLaunchKernelGGL((prefill_valu_kernel<K, V, bf16_t, bf16_t>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((valu_state_kernel<K, V, bf16_t, bf16_t>), grid, block, 0, st, a, recs, nslot);
     else
-        hipLaunchKernelGGL((prefill_valu_kernel<K, V, bf16_t, float>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((valu_state_kernel<K, V, bf16_t, float>), grid, block, 0, st, a, recs, nslot);
     return hipGetLastError();
 }
 
@@ -251,6 +354,12 @@ hipError_t launch_kv(const PrefillArgs &a, hipStream_t st) {
 
 hipError_t launch_epilogue(const PrefillArgs &a, hipStream_t st) {
     return a.V == 128 ? launch_epi<128>(a, st) : launch_epi<64>(a, st);
+}
+
+size_t prefill_valu_workspace(int32_t N, int32_t T, int32_t H, int32_t K) {
+    if (T <= 0) return 0;
+    const size_t rb = K == 128 ? ValuRec<128>::BYTES : ValuRec<64>::BYTES;
+    return valu_slots(T, N) * static_cast<size_t>(H) * rb;
 }
 
 hipError_t launch_prefill_valu(const PrefillArgs &a, hipStream_t st) {

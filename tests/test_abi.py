@@ -105,7 +105,9 @@ def test_workspace_query(lib):
     big = ws(16, 524288, 32, 128, 128, torch.bfloat16)
     assert big >= (524288 // 64) * 32 * 54 * 1024
     assert ws(1, 0, 4, 128, 128, torch.bfloat16) > 0          # offsets even without tokens
-    assert ws(1, 4096, 4, 128, 128, torch.float32) == 0       # the fp32 path needs none
+    # the fp32 path stages one fp32 record per (chunk, head): at least 128 KB each at d_k = 128
+    assert ws(1, 4096, 4, 128, 128, torch.float32) >= (4096 // 64) * 4 * 128 * 1024
+    assert ws(1, 0, 4, 128, 128, torch.float32) == 0          # no tokens, no records
     assert ws(1, 4096, 4, 96, 128, torch.bfloat16) == 0       # unsupported head dim
     assert ws(0, 4096, 4, 128, 128, torch.bfloat16) == 0      # invalid N
     # grows with the token count and the head count
