@@ -126,15 +126,18 @@ __global__ __launch_bounds__(kNT) void valu_prep_kernel(PrefillArgs a, char *rec
         sm.glast[tid] = acc;
     }
     __syncthreads();
-    for (int p = tid; p < kC * kC; p += kNT) {  // A and P, one (r, s) pair each
-        const int r = p / kC, s = p % kC;
+    // A and P on and below the diagonal, one (r, s) pair each: pair p = r (r + 1) / 2 + s
+    // (the entries above the diagonal are never read; the record gets zeros there)
+    for (int p = tid; p < kC * (kC + 1) / 2; p += kNT) {
+        int r = static_cast<int>((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
+        if ((r + 1) * (r + 2) / 2 <= p) ++r;  // float rounding, either way
+        if (r * (r + 1) / 2 > p) --r;
+        const int s = p - r * (r + 1) / 2;
         float aa = 0.f, pp = 0.f;
-        if (s <= r) {
-            for (int i = 0; i < K; ++i) {
-                const float ks = sm.KK[s * KP + i] * __expf(sm.G[r * KP + i] - sm.G[s * KP + i]);
-                aa = fmaf(sm.KK[r * KP + i], ks, aa);
-                pp = fmaf(sm.QQ[r * KP + i], ks, pp);
-            }
+        for (int i = 0; i < K; ++i) {
+            const float ks = sm.KK[s * KP + i] * __expf(sm.G[r * KP + i] - sm.G[s * KP + i]);
+            aa = fmaf(sm.KK[r * KP + i], ks, aa);
+            pp = fmaf(sm.QQ[r * KP + i], ks, pp);
         }
         sm.A[r * CP + s] = s < r ? sm.bet[r] * aa : 0.f;
         sm.P[r * CP + s] = pp;
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(kNT) void valu_prep_kernel(PrefillArgs a, char *rec
         const int r = p / kC, s = p % kC;
         const float t = s < r ? sm.A[r * CP + s] : (s == r ? 1.f : 0.f);
         tb[p] = t * sm.bet[s];
-        pm[p] = sm.P[r * CP + s];
+        pm[p] = s <= r ? sm.P[r * CP + s] : 0.f;
     }
     float *ke = reinterpret_cast<float *>(rec + R::KE), *qe = reinterpret_cast<float *>(rec + R::QE);
     float *kgn = reinterpret_cast<float *>(rec + R::KG);
@@ -223,21 +226,26 @@ __global__ __launch_bounds__(kNT) void valu_state_kernel(PrefillArgs a, const ch
         const char *rec = hrec + static_cast<size_t>(base + c) * R::BYTES;
         __syncthreads();
         {
-            const float *tb = reinterpret_cast<const float *>(rec + R::TB);
-            const float *pm = reinterpret_cast<const float *>(rec + R::P);
-            for (int p = tid; p < kC * kC; p += kNT) {
-                const int r = p / kC, s = p % kC;
-                sm.TB[r * CP + s] = tb[p];
-                sm.P[r * CP + s] = pm[p];
+            // 16-byte loads; the LDS rows are padded by one word, so the stores are single words
+            const float4 *tb = reinterpret_cast<const float4 *>(rec + R::TB);
+            const float4 *pm = reinterpret_cast<const float4 *>(rec + R::P);
+            for (int p = tid; p < kC * kC / 4; p += kNT) {
+                const int r = (4 * p) / kC, s = (4 * p) % kC;
+                const float4 x = tb[p], y = pm[p];
+                float *dt = &sm.TB[r * CP + s], *dp = &sm.P[r * CP + s];
+                dt[0] = x.x; dt[1] = x.y; dt[2] = x.z; dt[3] = x.w;
+                dp[0] = y.x; dp[1] = y.y; dp[2] = y.z; dp[3] = y.w;
             }
-            const float *ke = reinterpret_cast<const float *>(rec + R::KE);
-            const float *qe = reinterpret_cast<const float *>(rec + R::QE);
-            const float *kgn = reinterpret_cast<const float *>(rec + R::KG);
-            for (int idx = tid; idx < kC * K; idx += kNT) {
-                const int r = idx / K, i = idx % K;
-                sm.KE[r * KP + i] = ke[idx];
-                sm.QE[r * KP + i] = qe[idx];
-                sm.KG[r * KP + i] = kgn[idx];
+            const float4 *ke = reinterpret_cast<const float4 *>(rec + R::KE);
+            const float4 *qe = reinterpret_cast<const float4 *>(rec + R::QE);
+            const float4 *kgn = reinterpret_cast<const float4 *>(rec + R::KG);
+            for (int p = tid; p < kC * K / 4; p += kNT) {
+                const int r = (4 * p) / K, i = (4 * p) % K;
+                const float4 x = ke[p], y = qe[p], z = kgn[p];
+                float *d0 = &sm.KE[r * KP + i], *d1 = &sm.QE[r * KP + i], *d2 = &sm.KG[r * KP + i];
+                d0[0] = x.x; d0[1] = x.y; d0[2] = x.z; d0[3] = x.w;
+                d1[0] = y.x; d1[1] = y.y; d1[2] = y.z; d1[3] = y.w;
+                d2[0] = z.x; d2[1] = z.y; d2[2] = z.z; d2[3] = z.w;
             }
             if (tid < K) sm.gam[tid] = reinterpret_cast<const float *>(rec + R::GAM)[tid];
         }
