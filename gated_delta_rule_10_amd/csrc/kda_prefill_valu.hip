@@ -254,11 +254,20 @@ __global__ __launch_bounds__(kNT) void valu_state_kernel(PrefillArgs a, const ch
             sm.X[idx] = r < nt ? io<TIn>::load(vg + (static_cast<size_t>(t0 + r) * H + h) * V + j0 + cc) : 0.f;
         }
         __syncthreads();
-        for (int idx = tid; idx < kC * kVT; idx += kNT) {  // X = V - (K.e^G) S
-            const int r = idx / kVT, cc = idx % kVT;
-            float acc = 0.f;
-            for (int i = 0; i < K; ++i) acc = fmaf(sm.KE[r * KP + i], sm.S[i * kVT + cc], acc);
-            sm.X[idx] -= acc;
+        // Thread tid owns column cc = tid % 16 and the rows r0 + 16 m (m < NR) of the
+        // 64 x 16 products, so that one state (or U') value serves NR rows.
+        constexpr int NR = kC * kVT / kNT, NS = K * kVT / kNT;
+        static_assert(NR * kNT == kC * kVT && NS * kNT == K * kVT, "whole tiles per thread");
+        const int cc = tid % kVT, r0 = tid / kVT;
+        {  // X = V - (K.e^G) S
+            float acc[NR] = {};
+            for (int i = 0; i < K; ++i) {
+                const float sv = sm.S[i * kVT + cc];
+#pragma unroll
+                for (int m = 0; m < NR; ++m) acc[m] = fmaf(sm.KE[(r0 + 16 * m) * KP + i], sv, acc[m]);
+            }
+#pragma unroll
+            for (int m = 0; m < NR; ++m) sm.X[(r0 + 16 * m) * kVT + cc] -= acc[m];
         }
         __syncthreads();
         for (int idx = tid; idx < kC * kVT; idx += kNT) {  // U' = T Diag(beta) X
@@ -268,21 +277,36 @@ __global__ __launch_bounds__(kNT) void valu_state_kernel(PrefillArgs a, const ch
             sm.U[idx] = acc;
         }
         __syncthreads();
-        for (int idx = tid; idx < kC * kVT; idx += kNT) {  // O = (Q.e^G) S + P U'
-            const int r = idx / kVT, cc = idx % kVT;
-            if (r < nt) {
-                float acc = 0.f;
-                for (int i = 0; i < K; ++i) acc = fmaf(sm.QE[r * KP + i], sm.S[i * kVT + cc], acc);
-                for (int s = 0; s <= r; ++s) acc = fmaf(sm.P[r * CP + s], sm.U[s * kVT + cc], acc);
-                io<TOut>::store(og + (static_cast<size_t>(t0 + r) * H + h) * V + j0 + cc, a.scale * acc);
+        {  // O = (Q.e^G) S + P U' (P is zero above the diagonal)
+            float acc[NR] = {};
+            for (int i = 0; i < K; ++i) {
+                const float sv = sm.S[i * kVT + cc];
+#pragma unroll
+                for (int m = 0; m < NR; ++m) acc[m] = fmaf(sm.QE[(r0 + 16 * m) * KP + i], sv, acc[m]);
+            }
+            for (int s2 = 0; s2 < kC; ++s2) {
+                const float uv = sm.U[s2 * kVT + cc];
+#pragma unroll
+                for (int m = 0; m < NR; ++m) acc[m] = fmaf(sm.P[(r0 + 16 * m) * CP + s2], uv, acc[m]);
+            }
+#pragma unroll
+            for (int m = 0; m < NR; ++m) {
+                const int r = r0 + 16 * m;
+                if (r < nt) io<TOut>::store(og + (static_cast<size_t>(t0 + r) * H + h) * V + j0 + cc, a.scale * acc[m]);
             }
         }
         __syncthreads();
-        for (int idx = tid; idx < K * kVT; idx += kNT) {  // S <- e^{G_n} S + (K.e^{G_n-G})^T U'
-            const int i = idx / kVT, cc = idx % kVT;
-            float acc = sm.gam[i] * sm.S[idx];
-            for (int r = 0; r < kC; ++r) acc = fmaf(sm.KG[r * KP + i], sm.U[r * kVT + cc], acc);
-            sm.S[idx] = acc;
+        {  // S <- e^{G_n} S + (K.e^{G_n-G})^T U'; thread tid owns rows r0 + 16 m of S
+            float acc[NS];
+#pragma unroll
+            for (int m = 0; m < NS; ++m) acc[m] = sm.gam[r0 + 16 * m] * sm.S[(r0 + 16 * m) * kVT + cc];
+            for (int r = 0; r < kC; ++r) {
+                const float uv = sm.U[r * kVT + cc];
+#pragma unroll
+                for (int m = 0; m < NS; ++m) acc[m] = fmaf(sm.KG[r * KP + r0 + 16 * m], uv, acc[m]);
+            }
+#pragma unroll
+            for (int m = 0; m < NS; ++m) sm.S[(r0 + 16 * m) * kVT + cc] = acc[m];
         }
     }
     __syncthreads();
