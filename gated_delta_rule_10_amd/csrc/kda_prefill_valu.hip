@@ -125,22 +125,68 @@ __global__ __launch_bounds__(kNT) void valu_prep_kernel(PrefillArgs a, char *rec
         }
         sm.glast[tid] = acc;
     }
-    __syncthreads();
-    // A and P on and below the diagonal, one (r, s) pair each: pair p = r (r + 1) / 2 + s
-    // (the entries above the diagonal are never read; the record gets zeros there)
-    for (int p = tid; p < kC * (kC + 1) / 2; p += kNT) {
-        int r = static_cast<int>((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
-        if ((r + 1) * (r + 2) / 2 <= p) ++r;  // float rounding, either way
-        if (r * (r + 1) / 2 > p) --r;
-        const int s = p - r * (r + 1) / 2;
-        float aa = 0.f, pp = 0.f;
-        for (int i = 0; i < K; ++i) {
-            const float ks = sm.KK[s * KP + i] * __expf(sm.G[r * KP + i] - sm.G[s * KP + i]);
-            aa = fmaf(sm.KK[r * KP + i], ks, aa);
-            pp = fmaf(sm.QQ[r * KP + i], ks, pp);
+    // G never increases along the chunk, so e^{-G} stays below e^80 everywhere when the
+    // last row does: then e^{G_r - G_s} = e^{G_r} e^{-G_s} and A, P are plain products
+    const bool exact = __syncthreads_or(tid < K && sm.glast[tid] < -80.f);
+    if (!exact) {
+        // in place: k -> K.e^G, q -> Q.e^G, G -> K.e^{-G}
+        for (int idx = tid; idx < kC * K; idx += kNT) {
+            const int r = idx / K, i = idx % K;
+            const float G = sm.G[r * KP + i], e1 = __expf(G), e2 = __expf(-G);
+            const float kv = sm.KK[r * KP + i];
+            sm.KK[r * KP + i] = kv * e1;
+            sm.QQ[r * KP + i] *= e1;
+            sm.G[r * KP + i] = kv * e2;
         }
-        sm.A[r * CP + s] = s < r ? sm.bet[r] * aa : 0.f;
-        sm.P[r * CP + s] = pp;
+        __syncthreads();
+        // A = Diag(beta) strict_lower((K.e^G)(K.e^{-G})^T), P = lower((Q.e^G)(K.e^{-G})^T):
+        // thread tid owns the 4 x 4 tile of rows 4 (tid / 16) .., columns 4 (tid % 16) ..
+        const int rb = 4 * (tid / 16), cb = 4 * (tid % 16);
+        float aa[4][4] = {}, pp[4][4] = {};
+        if (cb <= rb + 3) {
+            for (int i = 0; i < K; ++i) {
+                float kr[4], qr[4], kc[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    kr[m] = sm.KK[(rb + m) * KP + i];
+                    qr[m] = sm.QQ[(rb + m) * KP + i];
+                    kc[m] = sm.G[(cb + m) * KP + i];
+                }
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+#pragma unroll
+                    for (int nn = 0; nn < 4; ++nn) {
+                        aa[m][nn] = fmaf(kr[m], kc[nn], aa[m][nn]);
+                        pp[m][nn] = fmaf(qr[m], kc[nn], pp[m][nn]);
+                    }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int nn = 0; nn < 4; ++nn) {
+                const int r = rb + m, s2 = cb + nn;
+                sm.A[r * CP + s2] = s2 < r ? sm.bet[r] * aa[m][nn] : 0.f;
+                sm.P[r * CP + s2] = s2 <= r ? pp[m][nn] : 0.f;
+            }
+    } else {
+        // a channel decays by more than e^80 over the chunk: e^{G_r - G_s} per element,
+        // A and P on and below the diagonal, one (r, s) pair each: p = r (r + 1) / 2 + s
+        // (the entries above the diagonal are never read; the record gets zeros there)
+        for (int p = tid; p < kC * (kC + 1) / 2; p += kNT) {
+            int r = static_cast<int>((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
+            if ((r + 1) * (r + 2) / 2 <= p) ++r;  // float rounding, either way
+            if (r * (r + 1) / 2 > p) --r;
+            const int s2 = p - r * (r + 1) / 2;
+            float aa = 0.f, pp = 0.f;
+            for (int i = 0; i < K; ++i) {
+                const float ks = sm.KK[s2 * KP + i] * __expf(sm.G[r * KP + i] - sm.G[s2 * KP + i]);
+                aa = fmaf(sm.KK[r * KP + i], ks, aa);
+                pp = fmaf(sm.QQ[r * KP + i], ks, pp);
+            }
+            sm.A[r * CP + s2] = s2 < r ? sm.bet[r] * aa : 0.f;
+            sm.P[r * CP + s2] = pp;
+        }
     }
     __syncthreads();
     // T = (I + A)^{-1}, row by row: T[r][c] = -sum_{c<=s<r} A[r][s] T[s][c],
@@ -167,12 +213,18 @@ __global__ __launch_bounds__(kNT) void valu_prep_kernel(PrefillArgs a, char *rec
     float *kgn = reinterpret_cast<float *>(rec + R::KG);
     for (int idx = tid; idx < kC * K; idx += kNT) {
         const int r = idx / K, i = idx % K;
-        const float G = sm.G[r * KP + i];
-        const float e1 = __expf(G), e2 = __expf(sm.glast[i] - G);
-        const float kv = sm.KK[r * KP + i];
-        ke[idx] = kv * e1;
-        qe[idx] = sm.QQ[r * KP + i] * e1;
-        kgn[idx] = kv * e2;
+        if (!exact) {  // the LDS holds K.e^G, Q.e^G and K.e^{-G}
+            ke[idx] = sm.KK[r * KP + i];
+            qe[idx] = sm.QQ[r * KP + i];
+            kgn[idx] = sm.G[r * KP + i] * __expf(sm.glast[i]);
+        } else {
+            const float G = sm.G[r * KP + i];
+            const float e1 = __expf(G), e2 = __expf(sm.glast[i] - G);
+            const float kv = sm.KK[r * KP + i];
+            ke[idx] = kv * e1;
+            qe[idx] = sm.QQ[r * KP + i] * e1;
+            kgn[idx] = kv * e2;
+        }
     }
     if (tid < K) reinterpret_cast<float *>(rec + R::GAM)[tid] = __expf(sm.glast[tid]);
 }

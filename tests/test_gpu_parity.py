@@ -72,9 +72,12 @@ def test_prefill_no_tokens_at_all(dt):
     assert torch.count_nonzero(sT).item() == 0
 
 
-def test_prefill_strong_decay():
-    """Large gate magnitudes (alpha down to ~e^-6 per token)."""
-    _prefill_case(inputs.prefill_inputs(9, [300], 2, 128, 128, "bf16", 3.0, "random"))
+@pytest.mark.parametrize("dt,decay", [("bf16", 3.0), ("f32", 3.0), ("f32", 1.0)])
+def test_prefill_strong_decay(dt, decay):
+    """Large gate magnitudes (alpha down to ~e^-6 per token). On the fp32 path,
+    decay 3.0 takes chunks past e^80 of total decay (the exact per-element form)
+    and decay 1.0 keeps them on the factorised form with factors up to ~e^45."""
+    _prefill_case(inputs.prefill_inputs(9, [300], 2, 128, 128, dt, decay, "random"))
 
 
 def test_prefill_null_vs_zero_state_alias_and_determinism():
