@@ -1,0 +1,99 @@
+"""Out-of-bounds writes: every output, state and workspace buffer sits between
+guard bands of a sentinel byte inside a larger allocation. After each call the
+bands must be untouched, and the results must equal those of a call on plain
+buffers, bit for bit."""
+
+import pytest
+import torch
+
+from gated_delta_rule_10_amd import inputs, kda
+from tests import gpu_common as gc
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 4096  # bytes on each side (keeps 16-byte alignment)
+SENTINEL = 0xA5
+
+
+class Guarded:
+    """A tensor of `shape` and `dtype` inside a byte buffer with guard bands."""
+
+    def __init__(self, shape, dtype, fill=None):
+        n = 1
+        for s in shape:
+            n *= s
+        nbytes = n * torch.tensor([], dtype=dtype).element_size()
+        self.buf = torch.full((GUARD + nbytes + GUARD,), SENTINEL, dtype=torch.uint8, device="cuda")
+        self.t = self.buf[GUARD:GUARD + nbytes].view(dtype).view(shape)
+        if fill is not None:
+            self.t.copy_(fill)
+
+    def intact(self):
+        return bool((self.buf[:GUARD] == SENTINEL).all()) and bool((self.buf[-GUARD:] == SENTINEL).all())
+
+
+def _prefill(d, dt, ex=None):
+    T, H, K = d["q"].shape
+    V = d["v"].shape[2]
+    N = d["cu_seqlens"].numel() - 1
+    tin = torch.bfloat16 if dt == "bf16" else torch.float32
+    od = torch.bfloat16 if dt == "bf16" else torch.float32
+    ws_n = kda.kda_chunk_fwd_workspace_size(N, T, H, K, V, tin)
+    o, fin, ws = Guarded((T, H, V), od), Guarded((N, H, K, V), torch.float32), Guarded((max(ws_n, 16),), torch.uint8)
+    if ex is None:
+        kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["cu_seqlens"],
+                          initial_state=d["initial_state"], final_state=fin.t, o=o.t, workspace=ws.t, out_dtype=od)
+        ro, rs = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["cu_seqlens"],
+                                   initial_state=d["initial_state"], out_dtype=od)
+    else:
+        kda.kda_chunk_fwd_ex(d["q"], d["k"], d["v"], d["cu_seqlens"], log_alpha=d["log_alpha"], beta=d["beta"],
+                             initial_state=d["initial_state"], final_state=fin.t, o=o.t, workspace=ws.t,
+                             out_dtype=od, **ex)
+        ro, rs = kda.kda_chunk_fwd_ex(d["q"], d["k"], d["v"], d["cu_seqlens"], log_alpha=d["log_alpha"],
+                                      beta=d["beta"], initial_state=d["initial_state"], out_dtype=od, **ex)
+    torch.cuda.synchronize()
+    for name, g in (("o", o), ("final_state", fin), ("workspace", ws)):
+        assert g.intact(), f"{name}: a guard band was written"
+    assert torch.equal(o.t, ro) and torch.equal(fin.t, rs)
+
+
+@pytest.mark.parametrize("seg,side", [(None, None), ("2", "1"), ("3", "0")])
+def test_prefill_bf16_writes_nothing_outside(seg, side, monkeypatch):
+    if seg is not None:
+        monkeypatch.setenv("KDA_SEG_CHUNKS", seg)
+        monkeypatch.setenv("KDA_SIDE_STREAM", side)
+    d = gc.to_device(inputs.prefill_inputs(41, [300, 0, 77, 1, 200], 3, 128, 128, "bf16", 0.1, "random"))
+    _prefill(d, "bf16")
+
+
+def test_prefill_bf16_epilogue_writes_nothing_outside(monkeypatch):
+    monkeypatch.setenv("KDA_SEG_CHUNKS", "2")
+    d = gc.to_device(inputs.prefill_inputs(42, [190, 64, 5], 2, 128, 64, "bf16", 0.1, "random"))
+    T, H, V = d["v"].shape
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(42)
+    z = torch.randn((T, H, V), generator=gen, device="cuda").to(torch.bfloat16)
+    nw = 1 + 0.1 * torch.randn((V,), generator=gen, device="cuda")
+    _prefill(d, "bf16", ex=dict(norm=True, norm_eps=1e-6, norm_weight=nw, out_gate=z, out_gate_act="sigmoid"))
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64)])
+def test_prefill_f32_writes_nothing_outside(dk, dv):
+    d = gc.to_device(inputs.prefill_inputs(43, [130, 0, 64, 3], 2, dk, dv, "f32", 0.1, "random"))
+    _prefill(d, "f32")
+
+
+def test_decode_writes_nothing_outside():
+    x = inputs.device_decode_inputs(44, 2, 5, 3, 128, 128, slots=9)
+    si = torch.tensor([7, 0, 4, 8, 2], dtype=torch.int32, device="cuda")
+    state = Guarded((9, 3, 128, 128), torch.float32, fill=x["state"])
+    ref_state = x["state"].clone()
+    for s in range(2):
+        # copies: a step's slice of a [steps, 5, 3] beta array need not be 16-byte aligned
+        q, k, v, g, b = (x[n][s].clone() for n in ("q", "k", "v", "log_alpha", "beta"))
+        o = Guarded((5, 3, 128), torch.bfloat16)
+        kda.kda_decode_step(q, k, v, g, b, state.t, si, o=o.t)
+        ro = kda.kda_decode_step(q, k, v, g, b, ref_state, si)
+        torch.cuda.synchronize()
+        assert o.intact() and state.intact(), "a guard band was written"
+        assert torch.equal(o.t, ro) and torch.equal(state.t, ref_state)
