@@ -34,6 +34,22 @@ bool force_valu() {
     return f;
 }
 
+// Debugging aid: KDA_DEBUG_SYNC=1 waits for each call's work, so that an error while
+// it runs is reported by that call (as KDA_ERR_HIP). Read once per process; not for
+// use under graph capture.
+bool debug_sync() {
+    static const bool f = [] {
+        const char *e = std::getenv("KDA_DEBUG_SYNC");
+        return e && std::strcmp(e, "1") == 0;
+    }();
+    return f;
+}
+hipError_t finish(hipError_t e, hipStream_t stream) {
+    if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(stream);
+    if (e == hipSuccess && debug_sync()) e = hipGetLastError();
+    return e;
+}
+
 }  // namespace
 
 namespace {
@@ -109,7 +125,7 @@ kda_status_t chunk_fwd(const void *q, const void *k, const void *v, const float 
         e = kda::launch_prefill_valu(a, stream);
         if (e == hipSuccess && epi && T_total > 0) e = kda::launch_epilogue(a, stream);
     }
-    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    return finish(e, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 kda_status_t decode_step(const void *q, const void *k, const void *v, const float *log_alpha, const float *beta,
@@ -137,7 +153,7 @@ kda_status_t decode_step(const void *q, const void *k, const void *v, const floa
     a.Hk = op.num_k_heads; a.gx = op.gate_x; a.by = op.beta_y; a.gscale = op.gate_scale;
     a.norm = op.norm != 0; a.eps = op.norm_eps; a.nw = op.norm_weight; a.z = op.out_gate;
     a.zact = op.out_gate_act;
-    return kda::launch_decode(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    return finish(kda::launch_decode(a, stream), stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 }  // namespace

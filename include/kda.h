@@ -41,7 +41,10 @@
  *    with the layouts given below (last dimension contiguous).
  *  - Arguments are validated on the host before anything is enqueued. A
  *    status other than KDA_OK means nothing was enqueued, except
- *    KDA_ERR_HIP, which reports a failed kernel launch.
+ *    KDA_ERR_HIP, which reports a failed kernel launch. With KDA_DEBUG_SYNC=1
+ *    in the environment (read once, a debugging aid, not for use under graph
+ *    capture) every call also waits for its work on `stream` and reports an
+ *    error while it ran as KDA_ERR_HIP.
  *  - Device-side contents are the caller's contract and are not checked:
  *    cu_seqlens must be non-decreasing from 0 to T_total, log_alpha finite
  *    and <= 0, slot indices distinct and in range. Stability of the
