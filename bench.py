@@ -139,15 +139,30 @@ def cpu_baseline_prefill(d, target_s=12.0):
         sub = {n: d[n][:tokens].float().cpu().numpy() for n in ("q", "k", "v", "log_alpha", "beta")}
         s0 = d["initial_state"].cpu().numpy()
         t0 = time.perf_counter()
-        oracle.prefill(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["beta"],
-                       np.array([0, tokens], np.int32), 1.0, s0, nthreads=threads)
+        ref = oracle.prefill(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["beta"],
+                             np.array([0, tokens], np.int32), 1.0, s0, nthreads=threads)
         elapsed = time.perf_counter() - t0
         if elapsed >= target_s / 2 or tokens >= d["q"].shape[0]:
             break
         tokens = min(d["q"].shape[0], int(tokens * max(2.0, min(16.0, target_s / max(elapsed, 1e-3)))))
-    return dict(value=tokens / elapsed / 1e6, unit="Mtokens/s", cores=threads, cpu=_cpu_model(), kind="oracle",
-                sample=f"fp64 oracle, first {tokens} tokens of the 128K sequence, all 32 heads, "
-                       f"{elapsed:.2f} s", seconds=elapsed)
+    out = dict(value=tokens / elapsed / 1e6, unit="Mtokens/s", cores=threads, cpu=_cpu_model(), kind="oracle",
+               sample=f"fp64 oracle, first {tokens} tokens of the 128K sequence, all 32 heads, "
+                      f"{elapsed:.2f} s", seconds=elapsed)
+    return out, (ref if tokens >= d["q"].shape[0] else None)
+
+
+def err_over_rms(got, ref, bf16_out):
+    """Max-abs error over RMS(ref); for bf16 outputs, the error beyond half a bf16
+    ulp of the value (rounding the exact value to bf16 alone costs that much)."""
+    import numpy as np
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    d = np.abs(got - ref)
+    if bf16_out:
+        ax = np.maximum(np.abs(ref), np.abs(got))
+        e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+        d = np.maximum(d - np.where(ax > 0, np.exp2(e - 8.0), 0.0), 0.0)
+    return float(d.max() / max(float(np.sqrt(np.mean(ref * ref))), 1e-30))
 
 
 def cpu_baseline_decode(d, target_s=5.0):
@@ -272,6 +287,8 @@ def main():
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    # the timed calls' own outputs (later variants reuse the buffers), for the parity check
+    gpu_out = None if args.no_cpu_baseline else (o.float().cpu(), sT.cpu())
     total_ms = ev[0].elapsed_time(ev[-1])
     ms = total_ms / args.steps
     mtok = T / (ms / 1e3) / 1e6
@@ -341,6 +358,7 @@ def main():
     cpu_d = None
     if not args.no_cpu_baseline:
         cpu_d = {n: d[n] for n in ("q", "k", "v", "log_alpha", "beta", "initial_state")}
+        cpu_d["gpu_o"], cpu_d["gpu_s"] = gpu_out
     del d, o, sT
 
     # ---- the same operator on the other prefill workloads: one 1,048,576-token
@@ -470,7 +488,14 @@ def main():
         del dd, state
 
     if cpu_d is not None:
-        result["cpu_baseline"] = cpu_baseline_prefill(cpu_d)
+        result["cpu_baseline"], ref = cpu_baseline_prefill(cpu_d)
+        if ref is not None:
+            result["parity"] = {
+                "o_err_over_rms": round(err_over_rms(cpu_d["gpu_o"].numpy(), ref[0], True), 6),
+                "final_state_err_over_rms": round(err_over_rms(cpu_d["gpu_s"].numpy(), ref[1], False), 6),
+                "tol": 2e-2, "sample": "the timed calls' outputs, all 32 heads and 131072 tokens, against the "
+                                      "fp64 oracle of the CPU baseline (bf16 o: error beyond half a bf16 ulp)"}
+    result["source_sha256"] = source_hash()  # the hash the profiles under profiles/ record
     print(json.dumps(result), flush=True)
 
 
