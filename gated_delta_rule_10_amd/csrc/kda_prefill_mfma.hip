@@ -683,18 +683,23 @@ __device__ __forceinline__ void dma4(const void *base, uint32_t voff, const char
 // with e^{G_n-G}, and T Diag(beta)), e^{G_n}, and (HASV) the 64 x V tile of V.
 // Tokens past the sequence end read the last token (finite; their columns of
 // T Diag(beta) are zero).
-template <int K, int V, bool FULL, bool HASV, int NW>
+// PART (with FULL): 0 = the whole record, 1 = only K.e^G and Q.e^G (copied early),
+// 2 = everything but K.e^G and Q.e^G.
+template <int K, int V, bool FULL, bool HASV, int NW, int PART = 0>
 __device__ __forceinline__ void copy_chunk(char *dst, const char *rec, const bf16_t *vg, int t0, int tend,
                                            int H, int h, int w, int l) {
     using R = Rec<K>;
     constexpr int NKX = 4 * (K / 32);
     constexpr int KG0 = static_cast<int>(R::KGT / 1024);
     constexpr int NF = FULL ? static_cast<int>(R::GAM / 1024) : NKX + 2 * (K / 16) + 6;
+    static_assert(PART == 0 || FULL, "parts of the full record only");
+    constexpr int F0 = PART == 2 ? KG0 : 0, F1 = PART == 1 ? KG0 : NF;
     const uint32_t lo = static_cast<uint32_t>(l) * 16u;
-    for (int f = w; f < NF; f += NW) {
+    for (int f = F0 + w; f < F1; f += NW) {
         const int fi = (FULL || f < NKX) ? f : f - NKX + KG0;
         dma16(rec + fi * 1024, lo, dst + fi * 1024);
     }
+    if (PART == 1) return;
     // e^{G_n} [K] fp32 in copies of 256 B
     static_assert(K % 64 == 0, "e^{G_n} span");
     if (w == NW - 1) {
@@ -927,6 +932,15 @@ __device__ __forceinline__ void run_segment(char *lb0, char *lb1, char *ftd, f4 
     static_assert(!TILE || EPI || NP * NT == kC * 2 * V / 16, "output tile pieces");
     static_assert(!EPI || TPR * kC == NT, "one 16-column piece of the fp32 tile per thread");
     using VT = VTile<V>;
+    // With bf16 output tiles (no epilogue, whose fp32 tile reuses that region), the
+    // K.e^G and Q.e^G fragments of chunk c + 2 are copied into chunk c's buffer as soon
+    // as chunk c has read them, and the rest at chunk c + 1: each copy wave then has
+    // exactly EW early copies in flight while it waits for chunk c + 1 (the vector-memory
+    // counter retires this wave's loads and stores in the order they were issued).
+    constexpr bool LA = OUT && TILE && !EPI && COPYV;
+    constexpr int EW = LA ? 8 * (K / 32) / CW : 0;
+    static_assert(!LA || (8 * (K / 32)) % CW == 0, "early copies spread evenly over the copy waves");
+    static_assert(EW <= 15, "early copies within the low vmcnt field");
     if (cb >= ce) return;
     f4 out[NB][4];
     if (w < CW) copy_chunk<K, V, OUT, COPYV, CW>(lb0, hrec + static_cast<size_t>(cb) * RB, vg, tbeg, tend, H, h, w, l);
@@ -992,7 +1006,10 @@ __device__ __forceinline__ void run_segment(char *lb0, char *lb1, char *ftd, f4 
     lds_cchar *const fb0 = frag_base(lb0, l), *const fb1 = frag_base(lb1, l);
     auto body = [&](char *cur, lds_cchar *fbc, char *oth, int c) {
         const int tc = tbeg + (c - cb) * kC;
-        wait_all();  // this wave's copies of chunk c, its stores and its LDS writes are done
+        // this wave's copies of chunk c, its stores and its LDS writes are done (the early
+        // copies of chunk c + 1, issued last, may still be in flight)
+        if (LA && c > cb && c + 1 < ce && w < CW) __builtin_amdgcn_s_waitcnt(EW);
+        else wait_all();
         wg_barrier();
         u4 pc[(EPI || NP == 0) ? 1 : NP];
         f4 fx[4];
@@ -1009,9 +1026,18 @@ __device__ __forceinline__ void run_segment(char *lb0, char *lb1, char *ftd, f4 
             wait_lds();
         }
         if (TILE) wg_barrier();  // every wave has read the previous output tile
-        if (c + 1 < ce && w < CW)
-            copy_chunk<K, V, OUT, COPYV, CW>(oth, hrec + static_cast<size_t>(c + 1) * RB, vg, tc + kC, tend, H, h, w,
-                                             l);
+        if (c + 1 < ce && w < CW) {
+            bool rest = false;  // chunk c + 1's K.e^G and Q.e^G went out during chunk c - 1
+            if constexpr (LA) {
+                rest = c > cb;
+                if (rest)
+                    copy_chunk<K, V, OUT, COPYV, CW, 2>(oth, hrec + static_cast<size_t>(c + 1) * RB, vg, tc + kC, tend,
+                                                        H, h, w, l);
+            }
+            if (!rest)
+                copy_chunk<K, V, OUT, COPYV, CW>(oth, hrec + static_cast<size_t>(c + 1) * RB, vg, tc + kC, tend, H, h,
+                                                 w, l);
+        }
         if (TILE && c > cb) {
             if (EPI) {
                 epi_store(fx, tc - kC);
@@ -1037,6 +1063,11 @@ __device__ __forceinline__ void run_segment(char *lb0, char *lb1, char *ftd, f4 
         ChunkStep<K, V, NB, OUT, HASV> st;
         if (active) st.part_a(cur, fbc, S, col0, l, r, g);
         if (TILE) wg_barrier();  // every wave has read K.e^G, Q.e^G and V of chunk c: the tile may go there
+        if constexpr (LA) {
+            if (c + 2 < ce && w < CW)
+                copy_chunk<K, V, OUT, COPYV, CW, 1>(cur, hrec + static_cast<size_t>(c + 2) * RB, vg, tc + 2 * kC, tend, H,
+                                                    h, w, l);
+        }
         if (active) st.part_b(cur, fbc, S, out, scale, g);
         if (OUT && active) {
 #pragma unroll
