@@ -1,6 +1,8 @@
 """GPU invariances between the library's own entry points, independent of the
 oracle: a packed variable-length batch equals its sequences run one call at a
-time, and T decode steps equal one prefill over the same T tokens.
+time, T decode steps equal one prefill over the same T tokens, and repeated
+calls give the same bits (a missing wait between the copies into LDS and their
+reads would show up as a changed result).
 """
 
 import numpy as np
@@ -75,3 +77,35 @@ def test_decode_steps_equal_prefill(dt):
     tol = gc.TOL_BF16 if dt == "bf16" else gc.TOL_F32
     gc.assert_close("o (decode vs prefill)", gc.host(od), gc.host(o).astype(np.float64), tol)
     gc.assert_close("state (decode vs prefill)", gc.host(state), gc.host(sT).astype(np.float64), tol)
+
+
+@pytest.mark.parametrize("name,seg,side,reps,epi", [
+    ("long_128k", None, None, 6, False),
+    ("mid_4x4k", "2", "1", 16, False),
+    ("mid_4x4k", "3", "0", 16, False),
+    ("mid_4x4k", "2", "1", 8, True),
+])
+def test_repeated_calls_are_bitwise_identical(name, seg, side, reps, epi, monkeypatch):
+    for key, val in (("KDA_SEG_CHUNKS", seg), ("KDA_SIDE_STREAM", side)):
+        if val is None:
+            monkeypatch.delenv(key, raising=False)
+        else:
+            monkeypatch.setenv(key, val)
+    d = inputs.device_workload_inputs(name)
+    ex = {}
+    if epi:
+        T, H, V = d["v"].shape
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(61)
+        ex = dict(norm=True, norm_eps=1e-6, norm_weight=1 + 0.1 * torch.randn((V,), generator=gen, device="cuda"),
+                  out_gate=torch.randn((T, H, V), generator=gen, device="cuda").to(torch.bfloat16),
+                  out_gate_act="sigmoid")
+
+    def call():
+        return kda.kda_chunk_fwd_ex(d["q"], d["k"], d["v"], d["cu_seqlens"], log_alpha=d["log_alpha"],
+                                    beta=d["beta"], initial_state=d["initial_state"], **ex)
+
+    o0, s0 = call()
+    for _ in range(reps - 1):
+        o, s = call()
+        assert torch.equal(o, o0) and torch.equal(s, s0)
