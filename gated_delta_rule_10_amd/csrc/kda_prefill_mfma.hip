@@ -607,8 +607,9 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
 // A workgroup covers all columns of one (segment, head) state (and of M); each
 // wave holds 16 columns x d_k rows in MFMA accumulators (four waves per SIMD in
 // the map pass, two in the output pass). A chunk's record is copied global -> LDS once per workgroup with
-// direct-to-LDS loads, one chunk ahead, into a two-buffer ring, so that no record
-// is streamed by more than one compute unit at a time; while one wave of a SIMD
+// direct-to-LDS loads, one chunk ahead, into a two-buffer ring (the output pass
+// starts K.e^G and Q.e^G of the chunk after next too), so that no record is
+// streamed by more than one compute unit at a time; while one wave of a SIMD
 // waits on the memory pipeline the other computes.
 
 typedef __attribute__((address_space(3))) void lds_void;
