@@ -101,8 +101,9 @@ kda_status_t chunk_fwd(const void *q, const void *k, const void *v, const float 
         return KDA_ERR_INVALID_ARG;
     if (!head_dim_ok(d_k) || !head_dim_ok(d_v) || chunk_size != 64) return KDA_ERR_UNSUPPORTED;
     if (!dtype_pair_ok(in_dtype, out_dtype)) return KDA_ERR_UNSUPPORTED;
-    // grid sizes are int32 on the device side
+    // grid sizes are int32 on the device side, and so are token counts rounded up to whole chunks
     if (static_cast<int64_t>(N) * H * 16 > INT32_MAX) return KDA_ERR_INVALID_ARG;
+    if (T_total > INT32_MAX - 64) return KDA_ERR_INVALID_ARG;
     if (static_cast<int64_t>(T_total) * H * (d_k > d_v ? d_k : d_v) > (int64_t(1) << 40))
         return KDA_ERR_INVALID_ARG;
     const size_t need = kda_chunk_fwd_workspace_size(N, T_total, H, d_k, d_v, in_dtype);
@@ -175,7 +176,8 @@ const char *kda_status_string(kda_status_t s) {
 
 size_t kda_chunk_fwd_workspace_size(int32_t N, int32_t T_total, int32_t H, int32_t d_k,
                                     int32_t d_v, kda_dtype_t in_dtype) {
-    if (N < 1 || H < 1 || T_total < 0 || !head_dim_ok(d_k) || !head_dim_ok(d_v)) return 0;
+    if (N < 1 || H < 1 || T_total < 0 || T_total > INT32_MAX - 64 || !head_dim_ok(d_k) || !head_dim_ok(d_v))
+        return 0;
     // both paths stage every chunk's state-independent operands in the workspace
     if (in_dtype == KDA_BF16 && !force_valu()) return kda::prefill_mfma_workspace(N, T_total, H, d_k, d_v);
     return kda::prefill_valu_workspace(N, T_total, H, d_k);

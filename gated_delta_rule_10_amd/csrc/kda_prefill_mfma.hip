@@ -1356,13 +1356,13 @@ int cu_count() {
 
 // Chunks per segment: enough segments to give every compute unit a (segment,
 // head) at this size, and at least 16 chunks each. KDA_SEG_CHUNKS overrides it
-// (tests of the segment bookkeeping at small sizes).
+// (tests of the segment bookkeeping at small sizes), up to the chunk count.
 int seg_chunks(int32_t N, int32_t T, int32_t H) {
+    const int64_t nc = (static_cast<int64_t>(T) + kC - 1) / kC + N;
     if (const char *e = std::getenv("KDA_SEG_CHUNKS")) {
         const int v = std::atoi(e);
-        if (v >= 1) return v;
+        if (v >= 1) return static_cast<int>(std::min<int64_t>(v, nc));
     }
-    const int64_t nc = (static_cast<int64_t>(T) + kC - 1) / kC + N;
     return static_cast<int>(std::max<int64_t>(16, (nc * H + 255) / 256));
 }
 
@@ -1372,7 +1372,7 @@ struct WsLayout {
     size_t nc, nseg, off, soff, recs, sin, mapn, mapm, bytes;
     WsLayout(int32_t N, int32_t T, int32_t H) {
         L = seg_chunks(N, T, H);
-        nc = static_cast<size_t>((T + kC - 1) / kC) + N;
+        nc = static_cast<size_t>((static_cast<int64_t>(T) + kC - 1) / kC) + N;
         nseg = (nc + L - 1) / L + N;
         off = 0;
         soff = align256(static_cast<size_t>(N + 1) * 4);

@@ -49,6 +49,11 @@
  *    cu_seqlens must be non-decreasing from 0 to T_total, log_alpha finite
  *    and <= 0, slot indices distinct and in range. Stability of the
  *    recurrence needs ||k_t|| <= 1 and beta_t in [0, 2].
+ *  - Test overrides, read from the environment: KDA_SEG_CHUNKS=n (at every
+ *    call) cuts the state passes of the bf16 prefill into segments of n
+ *    chunks (at most the chunk count), and KDA_PREFILL_KERNEL=valu (once per
+ *    process) runs bf16 inputs through the fp32 prefill kernels. The workspace
+ *    size depends on both: query it under the environment of the call.
  *  - Apart from that stream and its events, the library holds no global
  *    mutable state. Calls are thread-safe (prefill calls take a lock while
  *    they enqueue); calls on different streams that write the same memory race.
@@ -89,7 +94,8 @@ const char *kda_status_string(kda_status_t status);
 
 /*
  * Bytes of device workspace kda_chunk_fwd needs for these sizes; 0 means the
- * call may pass workspace = NULL. Pure function of its arguments.
+ * call may pass workspace = NULL (or the sizes are invalid). A function of its
+ * arguments and of the test overrides above.
  */
 size_t kda_chunk_fwd_workspace_size(int32_t N, int32_t T_total, int32_t H,
                                     int32_t d_k, int32_t d_v,
@@ -119,7 +125,8 @@ size_t kda_chunk_fwd_workspace_size(int32_t N, int32_t T_total, int32_t H,
  *   workspace   device scratch of workspace_bytes (may be NULL if the size
  *               query returns 0)
  *
- * Sizes: N >= 1, H >= 1, T_total >= 0, d_k and d_v in {64, 128}. With
+ * Sizes: N >= 1, H >= 1, 0 <= T_total <= 2^31 - 65, N H < 2^27,
+ * T_total H max(d_k, d_v) <= 2^40, d_k and d_v in {64, 128}. With
  * T_total = 0 the token arrays (q, k, v, log_alpha, beta, o) may be NULL.
  * dtype pairs: (F32 in, F32 out), (BF16 in, BF16 out), (BF16 in, F32 out).
  * Internal arithmetic: fp32 state and accumulation; the state is fp32 at

@@ -88,6 +88,8 @@ def _prefill(lib, **over):
     (dict(N=0), kda.KDA_ERR_INVALID_ARG),
     (dict(H=0), kda.KDA_ERR_INVALID_ARG),
     (dict(T=-1), kda.KDA_ERR_INVALID_ARG),
+    (dict(T=2**31 - 64, H=1, dk=64, dv=64), kda.KDA_ERR_INVALID_ARG),  # whole chunks past int32
+    (dict(N=2**26, H=2), kda.KDA_ERR_INVALID_ARG),                      # N H 16 past int32
     (dict(din=7), kda.KDA_ERR_INVALID_ARG),
     (dict(dk=96), kda.KDA_ERR_UNSUPPORTED),
     (dict(dv=256), kda.KDA_ERR_UNSUPPORTED),
@@ -110,6 +112,8 @@ def test_workspace_query(lib):
     assert ws(1, 0, 4, 128, 128, torch.float32) == 0          # no tokens, no records
     assert ws(1, 4096, 4, 96, 128, torch.bfloat16) == 0       # unsupported head dim
     assert ws(0, 4096, 4, 128, 128, torch.bfloat16) == 0      # invalid N
+    assert ws(1, 2**31 - 64, 1, 64, 64, torch.bfloat16) == 0  # token count past the limit
+    assert ws(1, 2**31 - 65, 1, 64, 64, torch.bfloat16) >= (2**31 // 64) * 24 * 1024  # the largest allowed
     # grows with the token count and the head count
     assert ws(1, 8192, 4, 128, 128, torch.bfloat16) > ws(1, 4096, 4, 128, 128, torch.bfloat16)
     assert ws(1, 4096, 8, 128, 128, torch.bfloat16) > ws(1, 4096, 4, 128, 128, torch.bfloat16)

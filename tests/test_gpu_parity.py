@@ -99,12 +99,13 @@ def test_prefill_null_vs_zero_state_alias_and_determinism():
     assert torch.equal(o4, o5) and torch.equal(s4, st)
 
 
-@pytest.mark.parametrize("seg", ["1", "2", "3"])
+@pytest.mark.parametrize("seg", ["1", "2", "3", "2147483647"])
 def test_prefill_segmented_state_pass(seg, monkeypatch):
     """The state pass cut into segments of `seg` chunks (map pass with the first
     segments' output pass beside it on the second stream, prefix over segments,
     output pass) on ragged packed sequences, including empty ones, with a random
-    initial state; final_state aliasing initial_state."""
+    initial state; final_state aliasing initial_state. The largest override is
+    cut to the chunk count (one segment per sequence)."""
     monkeypatch.setenv("KDA_SEG_CHUNKS", seg)
     monkeypatch.setenv("KDA_SIDE_STREAM", "1")
     inp = inputs.prefill_inputs(11, [0, 700, 64, 1, 389, 0, 200], 3, 128, 128, "bf16", 0.1, "random")
