@@ -106,6 +106,28 @@ def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
     return t
 
 
+def _out(o: Optional[torch.Tensor], shape, dtype: torch.dtype, device) -> torch.Tensor:
+    """The output tensor: a new one, or the caller's after checking its shape and dtype
+    (the kernels write every element of that shape)."""
+    if o is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if tuple(o.shape) != tuple(shape) or o.dtype != dtype:
+        raise ValueError(f"o must be {dtype} {tuple(shape)}")
+    return _dev(o, "o")
+
+
+def _workspace(lib, workspace: Optional[torch.Tensor], N, T, H, d_k, d_v, in_dtype, device):
+    """(workspace, bytes): the caller's (on the GPU; the library checks its size) or a new
+    one of the size the library asks for (none when it asks for 0 bytes)."""
+    if workspace is None:
+        need = int(lib.kda_chunk_fwd_workspace_size(N, T, H, d_k, d_v, _code(in_dtype)))
+        if not need:
+            return None, 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    _dev(workspace, "workspace")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
 def _stream(stream) -> ctypes.c_void_p:
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -144,11 +166,7 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             or cu_seqlens.dtype != torch.int32:
         raise ValueError("log_alpha and beta must be float32, cu_seqlens int32")
     out_dtype = q.dtype if out_dtype is None else out_dtype
-    if o is None:
-        o = torch.empty((T, H, d_v), dtype=out_dtype, device=q.device)
-    elif o.shape != (T, H, d_v) or o.dtype != out_dtype:
-        raise ValueError("o has the wrong shape or dtype")
-    _dev(o, "o")
+    o = _out(o, (T, H, d_v), out_dtype, q.device)
     if initial_state is not None:
         _dev(initial_state, "initial_state")
         if initial_state.shape != (N, H, d_k, d_v) or initial_state.dtype != torch.float32:
@@ -159,11 +177,7 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         _dev(final_state, "final_state")
         if final_state.shape != (N, H, d_k, d_v) or final_state.dtype != torch.float32:
             raise ValueError("final_state must be float32 [N, H, d_k, d_v]")
-    if workspace is None:
-        need = int(lib.kda_chunk_fwd_workspace_size(N, T, H, d_k, d_v, _code(q.dtype)))
-        if need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    workspace, ws_bytes = _workspace(lib, workspace, N, T, H, d_k, d_v, q.dtype, q.device)
     st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
                            _ptr(cu_seqlens), N, T, H, d_k, d_v, _code(q.dtype),
                            _code(out_dtype), float(scale), _ptr(initial_state),
@@ -200,9 +214,7 @@ def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         if slot_idx.dtype != torch.int32 or slot_idx.shape != (B,):
             raise ValueError("slot_idx must be int32 [B]")
     out_dtype = q.dtype if out_dtype is None else out_dtype
-    if o is None:
-        o = torch.empty((B, H, d_v), dtype=out_dtype, device=q.device)
-    _dev(o, "o")
+    o = _out(o, (B, H, d_v), out_dtype, q.device)
     st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
                              _ptr(state_cache), _ptr(slot_idx), _ptr(o), B, H, d_k, d_v,
                              state_cache.shape[0], _code(q.dtype), _code(out_dtype),
@@ -285,9 +297,7 @@ def kda_chunk_fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqle
             if tuple(t.shape) != shape or t.dtype != dt:
                 raise ValueError(f"{name} must be {dt} {shape}")
     out_dtype = q.dtype if out_dtype is None else out_dtype
-    if o is None:
-        o = torch.empty((T, H, d_v), dtype=out_dtype, device=q.device)
-    _dev(o, "o")
+    o = _out(o, (T, H, d_v), out_dtype, q.device)
     num_slots = 0
     if state_slots is not None:
         _dev(state_slots, "state_slots")
@@ -309,11 +319,7 @@ def kda_chunk_fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqle
                 raise ValueError(f"{name} must be float32 [{'slots' if state_slots is not None else 'N'}, H, d_k, d_v]")
     op = _options(H, Hk, gate_x, beta_y, gate_scale, norm, norm_eps, norm_weight, out_gate, out_gate_act,
                   state_slots, num_slots)
-    if workspace is None:
-        need = int(lib.kda_chunk_fwd_workspace_size(N, T, H, d_k, d_v, _code(q.dtype)))
-        if need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    workspace, ws_bytes = _workspace(lib, workspace, N, T, H, d_k, d_v, q.dtype, q.device)
     st = lib.kda_chunk_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(cu_seqlens),
                               N, T, H, d_k, d_v, _code(q.dtype), _code(out_dtype), float(scale),
                               _ptr(initial_state), _ptr(final_state), _ptr(o), CHUNK_SIZE,
@@ -357,9 +363,7 @@ def kda_decode_step_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state_
         if slot_idx.dtype != torch.int32 or slot_idx.shape != (B,):
             raise ValueError("slot_idx must be int32 [B]")
     out_dtype = q.dtype if out_dtype is None else out_dtype
-    if o is None:
-        o = torch.empty((B, H, d_v), dtype=out_dtype, device=q.device)
-    _dev(o, "o")
+    o = _out(o, (B, H, d_v), out_dtype, q.device)
     op = _options(H, Hk, gate_x, beta_y, gate_scale, norm, norm_eps, norm_weight, out_gate, out_gate_act)
     st = lib.kda_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(state_cache),
                                 _ptr(slot_idx), _ptr(o), B, H, d_k, d_v, state_cache.shape[0],
