@@ -128,8 +128,18 @@ def _workspace(lib, workspace: Optional[torch.Tensor], N, T, H, d_k, d_v, in_dty
     return workspace, workspace.numel() * workspace.element_size()
 
 
-def _stream(stream) -> ctypes.c_void_p:
-    s = torch.cuda.current_stream() if stream is None else stream
+def _one_device(device, *tensors) -> None:
+    """Every tensor given (None skipped) on `device`: the call runs there."""
+    for t in tensors:
+        if t is not None and t.device != device:
+            raise ValueError(f"all tensors must be on {device} (found one on {t.device})")
+
+
+def _stream(stream, device) -> ctypes.c_void_p:
+    """The stream to enqueue on: the given one (of `device`), else the current one of `device`."""
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    if s.device != device:
+        raise ValueError(f"stream is on {s.device}, the tensors on {device}")
     return ctypes.c_void_p(s.cuda_stream)
 
 
@@ -178,11 +188,13 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         if final_state.shape != (N, H, d_k, d_v) or final_state.dtype != torch.float32:
             raise ValueError("final_state must be float32 [N, H, d_k, d_v]")
     workspace, ws_bytes = _workspace(lib, workspace, N, T, H, d_k, d_v, q.dtype, q.device)
-    st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                           _ptr(cu_seqlens), N, T, H, d_k, d_v, _code(q.dtype),
-                           _code(out_dtype), float(scale), _ptr(initial_state),
-                           _ptr(final_state), _ptr(o), int(chunk_size), _ptr(workspace),
-                           ws_bytes, _stream(stream))
+    _one_device(q.device, k, v, log_alpha, beta, cu_seqlens, initial_state, final_state, o, workspace)
+    with torch.cuda.device(q.device):
+        st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                               _ptr(cu_seqlens), N, T, H, d_k, d_v, _code(q.dtype),
+                               _code(out_dtype), float(scale), _ptr(initial_state),
+                               _ptr(final_state), _ptr(o), int(chunk_size), _ptr(workspace),
+                               ws_bytes, _stream(stream, q.device))
     if st != KDA_OK:
         raise KDAError(st, "kda_chunk_fwd")
     return o, final_state
@@ -215,10 +227,12 @@ def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             raise ValueError("slot_idx must be int32 [B]")
     out_dtype = q.dtype if out_dtype is None else out_dtype
     o = _out(o, (B, H, d_v), out_dtype, q.device)
-    st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                             _ptr(state_cache), _ptr(slot_idx), _ptr(o), B, H, d_k, d_v,
-                             state_cache.shape[0], _code(q.dtype), _code(out_dtype),
-                             float(scale), _stream(stream))
+    _one_device(q.device, k, v, log_alpha, beta, state_cache, slot_idx, o)
+    with torch.cuda.device(q.device):
+        st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                 _ptr(state_cache), _ptr(slot_idx), _ptr(o), B, H, d_k, d_v,
+                                 state_cache.shape[0], _code(q.dtype), _code(out_dtype),
+                                 float(scale), _stream(stream, q.device))
     if st != KDA_OK:
         raise KDAError(st, "kda_decode_step")
     return o
@@ -320,10 +334,13 @@ def kda_chunk_fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqle
     op = _options(H, Hk, gate_x, beta_y, gate_scale, norm, norm_eps, norm_weight, out_gate, out_gate_act,
                   state_slots, num_slots)
     workspace, ws_bytes = _workspace(lib, workspace, N, T, H, d_k, d_v, q.dtype, q.device)
-    st = lib.kda_chunk_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(cu_seqlens),
-                              N, T, H, d_k, d_v, _code(q.dtype), _code(out_dtype), float(scale),
-                              _ptr(initial_state), _ptr(final_state), _ptr(o), CHUNK_SIZE,
-                              _ptr(workspace), ws_bytes, ctypes.byref(op), _stream(stream))
+    _one_device(q.device, k, v, cu_seqlens, log_alpha, beta, gate_x, beta_y, norm_weight, out_gate, state_slots,
+                initial_state, final_state, o, workspace)
+    with torch.cuda.device(q.device):
+        st = lib.kda_chunk_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(cu_seqlens),
+                                  N, T, H, d_k, d_v, _code(q.dtype), _code(out_dtype), float(scale),
+                                  _ptr(initial_state), _ptr(final_state), _ptr(o), CHUNK_SIZE,
+                                  _ptr(workspace), ws_bytes, ctypes.byref(op), _stream(stream, q.device))
     if st != KDA_OK:
         raise KDAError(st, "kda_chunk_fwd_ex")
     return o, final_state
@@ -365,10 +382,12 @@ def kda_decode_step_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state_
     out_dtype = q.dtype if out_dtype is None else out_dtype
     o = _out(o, (B, H, d_v), out_dtype, q.device)
     op = _options(H, Hk, gate_x, beta_y, gate_scale, norm, norm_eps, norm_weight, out_gate, out_gate_act)
-    st = lib.kda_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(state_cache),
-                                _ptr(slot_idx), _ptr(o), B, H, d_k, d_v, state_cache.shape[0],
-                                _code(q.dtype), _code(out_dtype), float(scale), ctypes.byref(op),
-                                _stream(stream))
+    _one_device(q.device, k, v, state_cache, slot_idx, log_alpha, beta, gate_x, beta_y, norm_weight, out_gate, o)
+    with torch.cuda.device(q.device):
+        st = lib.kda_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(state_cache),
+                                    _ptr(slot_idx), _ptr(o), B, H, d_k, d_v, state_cache.shape[0],
+                                    _code(q.dtype), _code(out_dtype), float(scale), ctypes.byref(op),
+                                    _stream(stream, q.device))
     if st != KDA_OK:
         raise KDAError(st, "kda_decode_step_ex")
     return o
