@@ -196,3 +196,18 @@ def test_binding_refuses_host_tensors(lib):
     x = torch.zeros((4, 2, 64))
     with pytest.raises(ValueError):
         kda.kda_chunk_fwd(x, x, x, x, torch.zeros((4, 2)), torch.zeros(2, dtype=torch.int32))
+
+
+def test_binding_helpers_refuse_mixed_devices_and_wrong_outputs():
+    """Host-side checks of the Python binding, without a GPU: tensors on another
+    device than the call's, and a caller's output of the wrong shape or dtype."""
+    import torch
+    from gated_delta_rule_10_amd import kda as kb
+    dev = torch.device("cuda", 0)
+    with pytest.raises(ValueError, match="all tensors must be on"):
+        kb._one_device(dev, None, torch.empty(2))
+    kb._one_device(torch.device("cpu"), None, torch.empty(2))  # same device: accepted
+    with pytest.raises(ValueError, match=r"o must be torch.bfloat16 \(4, 2, 8\)"):
+        kb._out(torch.empty((4, 2, 7), dtype=torch.bfloat16), (4, 2, 8), torch.bfloat16, dev)
+    with pytest.raises(ValueError, match="o must be"):
+        kb._out(torch.empty((4, 2, 8), dtype=torch.float32), (4, 2, 8), torch.bfloat16, dev)
