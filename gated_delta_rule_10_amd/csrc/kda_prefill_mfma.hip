@@ -1228,13 +1228,20 @@ __global__ __launch_bounds__(64 * (K + V) / (16 * kSegNB)) void seg_kernel(Prefi
 // reads. The output pass writes final states (which may alias the initial
 // states) while other segments of it still run, and its segment-0 workgroups may
 // run beside the map pass, so they read this copy.
+// Each state is copied by kSeedParts workgroups, so that a few long sequences still
+// spread the copies over many compute units.
+constexpr int kSeedParts = 16;
 template <int K, int V>
 __global__ __launch_bounds__(256) void seed_kernel(PrefillArgs a, const int32_t *soff, SegBufs sb) {
-    const int n = blockIdx.x / a.H, h = blockIdx.x - (blockIdx.x / a.H) * a.H;
+    constexpr int NQ = K * V / 4, PQ = NQ / kSeedParts;  // float4 per state, per part
+    static_assert(NQ % kSeedParts == 0, "whole parts");
+    const int item = blockIdx.x / kSeedParts, part = blockIdx.x - item * kSeedParts;
+    const int n = item / a.H, h = item - (item / a.H) * a.H;
     if (n >= a.N || soff[n + 1] - soff[n] < 2) return;
     const float4 *src = reinterpret_cast<const float4 *>(state_in(a, n, h));
     float4 *dst = reinterpret_cast<float4 *>(sb.sin + (static_cast<size_t>(soff[n]) * a.H + h) * K * V);
-    for (int i = threadIdx.x; i < K * V / 4; i += 256) dst[i] = src ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = part * PQ + static_cast<int>(threadIdx.x); i < (part + 1) * PQ; i += 256)
+        dst[i] = src ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 // S_in(g + 1) = M_g S_in(g) + N_g for the middle segments g of one (sequence, head),
@@ -1450,7 +1457,8 @@ hipError_t launch_kv(const PrefillArgs &a, hipStream_t st) {
     const size_t units = lay.nseg * a.H;
     if (maxc <= lay.L) return launch_out<K, V>(a, off, soff, lay.L, recs, sb, units, 2, st);
 
-    hipLaunchKernelGGL((seed_kernel<K, V>), dim3(static_cast<unsigned>(a.N) * a.H), dim3(256), 0, st, a, soff, sb);
+    hipLaunchKernelGGL((seed_kernel<K, V>), dim3(static_cast<unsigned>(a.N) * a.H * kSeedParts), dim3(256), 0, st, a,
+                       soff, sb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // The second stream only pays when the output pass needs more than one round
