@@ -46,8 +46,8 @@
 // exactly the set of rows a lane holds of two stacked 16x16 results, so a
 // product's result feeds the next product's B operand from registers.
 #include <algorithm>
+#include <atomic>
 #include <cstdlib>
-#include <mutex>
 #include <type_traits>
 
 #include "kda_device.h"
@@ -62,6 +62,9 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 constexpr int kC = 64;
 constexpr float kFastRange = 10.f;  // max decay exponent of one sub-chunk on the fp16 path
+// Bound of the fp16 diagonal column operand k_s e^{G_b - G_s} (<= max|k| e^{decay of the
+// sub-chunk}), below the fp16 maximum 65504; above it the exact fp32 path is taken.
+constexpr float kFastOperand = 3.0e4f;
 
 __device__ __forceinline__ f4 mfma(half8 a, half8 b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -178,8 +181,10 @@ struct PrepSmem {
     // columns 4s + g) both spread a wave's 64 lanes over distinct banks
     static constexpr int NCB = K / 32, LD = 68;
     float tot[4][K];       // decay of each sub-chunk per channel (log, <= 0)
-    float fac[16][K + 4];  // per-channel factors, see prep_kernel
+    float mid[4][K];       // decay from each sub-chunk's start through its 8th token (log, <= 0)
+    float fac[19][K + 4];  // per-channel factors, see prep_kernel
     float beta[kC];
+    float kmax[4];  // max |k_i|, |q_i| over the tokens and channels of each sub-chunk
     union {
         struct {
             half8 colv[10][NCB][64];  // B operands of the pairwise products
@@ -288,6 +293,19 @@ struct PrepRaw {
             }
         }
     }
+    // max |k_i|, |q_i| of the loaded channels, from the bf16 bits (sign cleared, two values
+    // per word compared as 16-bit integers, whose order is that of the magnitudes)
+    __device__ __forceinline__ float absmax() const {
+        typedef uint16_t us2 __attribute__((ext_vector_type(2)));
+        us2 m = {0, 0};
+#pragma unroll
+        for (int cb = 0; cb < K / 32; ++cb) {
+            const uint32_t w[8] = {kv[cb].x, kv[cb].y, kv[cb].z, kv[cb].w, qv[cb].x, qv[cb].y, qv[cb].z, qv[cb].w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, w[i] & 0x7FFF7FFFu));
+        }
+        return __uint_as_float(static_cast<uint32_t>(m.x > m.y ? m.x : m.y) << 16);
+    }
     // k, q and the inclusive scan of the log decay over the 16-token sub-chunk
     // (lanes r of a 16-lane row are its consecutive tokens), channels in chain order
     __device__ __forceinline__ void unpack(float (&kx)[K / 32][8], float (&qx)[K / 32][8], float (&sc)[K / 32][8],
@@ -360,6 +378,7 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
     PrepRaw<K, GX> raw;
     raw.load(a, nx, u < total, tr, g);
     raw.activate(a.gscale);
+    float kqmax = raw.absmax();  // of the item whose inputs the registers hold
     for (; u < total; u += gridDim.x) {
     const PrepItem it = nx;
     const int c = it.c, h = it.h;
@@ -368,32 +387,83 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
     float kx[NCB][8], qx[NCB][8], s[NCB][8];
     raw.unpack(kx, qx, s, a.gscale);
     if (g == 0) sm.beta[tr] = raw.beta(a);
-    if (r == 15) {
+    {  // max |k_i|, |q_i| of this sub-chunk: the lane's (taken when its loads landed), over
+       // its 16-lane row, then the 4 rows
+        float m = kqmax;
+        m = fmaxf(m, dpp_row_shr<1>(m));
+        m = fmaxf(m, dpp_row_shr<2>(m));
+        m = fmaxf(m, dpp_row_shr<4>(m));
+        m = fmaxf(m, dpp_row_shr<8>(m));
+        m = col_max(m);
+        if (l == 15) sm.kmax[w] = m;
+    }
+    if (r == 15 || r == 7) {
+        float(*dst)[K] = r == 15 ? sm.tot : sm.mid;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sm.tot[w][32 * cb + kidx(g, e)] = s[cb][e];
+            for (int e = 0; e < 8; ++e) dst[w][32 * cb + kidx(g, e)] = s[cb][e];
     }
     __syncthreads();
 
-    // ---- per-channel factors: 0..3 e^{G_{b_w}} (decay before sub-chunk w), 4..7 decay after
-    // sub-chunk w to the chunk end, 8..11 inverse decay of sub-chunk w (clamped; fast path
-    // only), 12 e^{tot1}, 13 e^{tot1+tot2}, 14 e^{tot2} (between sub-chunks), 15 e^{G_n}
-    int bad = 0;
-    if (tid < K) {
-        const float d0 = sm.tot[0][tid], d1 = sm.tot[1][tid], d2 = sm.tot[2][tid], d3 = sm.tot[3][tid];
-        float f[16];
-        f[0] = 1.f; f[1] = __expf(d0); f[2] = __expf(d0 + d1); f[3] = __expf(d0 + d1 + d2);
-        f[4] = __expf(d1 + d2 + d3); f[5] = __expf(d2 + d3); f[6] = __expf(d3); f[7] = 1.f;
-        f[8] = __expf(fminf(-d0, 80.f)); f[9] = __expf(fminf(-d1, 80.f));
-        f[10] = __expf(fminf(-d2, 80.f)); f[11] = __expf(fminf(-d3, 80.f));
-        f[12] = __expf(d1); f[13] = __expf(d1 + d2); f[14] = __expf(d2);
-        f[15] = __expf(d0 + d1 + d2 + d3);
+    // ---- per-channel factors. The pairwise products of a row in sub-chunk i take their
+    // reference at m_i, after the 8th token of sub-chunk i: e^{G_r - G_s} =
+    // e^{G_r - G_{m_i}} e^{G_{m_i} - G_s}, so both factors of a diagonal block stay within
+    // e^{(decay over 8 tokens)}, and every column factor of a block below it is <= 1. A
+    // chunk on the exact diagonal path (slow) takes the reference at the sub-chunk start
+    // instead (mu = 0 below), which keeps every row operand <= |k|.
+    // Rows, with mu_w the reference's decay inside sub-chunk w: 0..3 e^{G_{b_w} + mu_w}
+    // (K.e^G and Q.e^G from the row operands), 4..7 decay after sub-chunk w to the chunk
+    // end, 8..11 e^{mu_w - tot_w} (diagonal column operand, clamped), 12..14 e^{mu_{w+1}},
+    // 15..16 e^{tot_{w+1} + mu_{w+2}}, 17 e^{tot1 + tot2 + mu_3} (column operands of the
+    // blocks below the diagonal), 18 e^{G_n}.
+    // Two threads per channel, each with half of the rows. The first also checks whether
+    // the fast path applies: every sub-chunk's decay within e^kFastRange, and its fp16
+    // operands within range: a row operand (k or q times e^{G_r - G_m}) is at most
+    // max|k, q| e^{-mu}, a diagonal column operand at most max|k| e^{mu - tot}.
+    auto factors = [&](bool start_ref) {
+        int bad = 0;
+        if (tid < 2 * K) {
+            const int ch = tid & (K - 1);
+            const float d0 = sm.tot[0][ch], d1 = sm.tot[1][ch], d2 = sm.tot[2][ch], d3 = sm.tot[3][ch];
+            float mu[4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sm.fac[i][tid] = f[i];
-        bad = fmaxf(fmaxf(-d0, -d1), fmaxf(-d2, -d3)) > kFastRange;
-    }
+            for (int i = 0; i < 4; ++i) mu[i] = start_ref ? 0.f : sm.mid[i][ch];
+            if (tid < K) {
+                float emu[4], fd[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    emu[i] = __expf(mu[i]);
+                    fd[i] = __expf(fminf(mu[i] - (i == 0 ? d0 : i == 1 ? d1 : i == 2 ? d2 : d3), 80.f));
+                    sm.fac[8 + i][ch] = fd[i];
+                    if (i > 0) sm.fac[11 + i][ch] = emu[i];
+                    const float d = i == 0 ? d0 : i == 1 ? d1 : i == 2 ? d2 : d3;
+                    bad |= -d > kFastRange || !(sm.kmax[i] <= kFastOperand * emu[i]) ||
+                           !(sm.kmax[i] * fd[i] <= kFastOperand);
+                }
+                sm.fac[0][ch] = emu[0];
+            } else {
+                sm.fac[1][ch] = __expf(d0 + mu[1]);
+                sm.fac[2][ch] = __expf(d0 + d1 + mu[2]);
+                sm.fac[3][ch] = __expf(d0 + d1 + d2 + mu[3]);
+                sm.fac[4][ch] = __expf(d1 + d2 + d3);
+                sm.fac[5][ch] = __expf(d2 + d3);
+                sm.fac[6][ch] = __expf(d3);
+                sm.fac[7][ch] = 1.f;
+                sm.fac[15][ch] = __expf(d1 + mu[2]);
+                sm.fac[16][ch] = __expf(d2 + mu[3]);
+                sm.fac[17][ch] = __expf(d1 + d2 + mu[3]);
+                sm.fac[18][ch] = __expf(d0 + d1 + d2 + d3);
+            }
+        }
+        return bad;
+    };
+    const int bad = factors(false);
     const bool slow = __syncthreads_or(bad);
+    if (slow) {  // rare: the exact diagonal path, with the reference at the sub-chunk starts
+        (void)factors(true);
+        __syncthreads();
+    }
 
     // ---- elementwise: decayed operands
     half8 kr[NCB], qr[NCB];
@@ -410,17 +480,21 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
         half8 kexp, qg, cv0, cv1, cv2, cv3;
-        float tw[8], fb[8], fa[8], fi[8], f2[8], f3[8];
+        float tw[8], mw[8], fb[8], fa[8], fi[8], f1[8], f2[8], f3[8];
         row8(sm.tot[w], cb, tw);
+        row8(sm.mid[w], cb, mw);
         row8(sm.fac[w], cb, fb);
         row8(sm.fac[4 + w], cb, fa);
         row8(sm.fac[8 + w], cb, fi);
-        row8(sm.fac[w == 0 ? 12 : 14], cb, f2);
-        row8(sm.fac[13], cb, f3);
+        row8(sm.fac[12 + min(w, 2)], cb, f1);
+        row8(sm.fac[w == 0 ? 15 : 16], cb, f2);
+        row8(sm.fac[17], cb, f3);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int ch = 32 * cb + kidx(g, e);
-            const float rho = __expf(s[cb][e]);          // e^{G_r - G_b} <= 1
+            // e^{G_r - G_m} (m: the reference of this row's products; at most e^{8-token decay}
+            // on the fast path, <= 1 from the sub-chunk start on the slow path)
+            const float rho = __expf(s[cb][e] - (slow ? 0.f : mw[e]));
             const float tau = __expf(tw[e] - s[cb][e]);  // e^{G_{b'} - G_r} <= 1, b' = sub-chunk end
             const float krv = kx[cb][e] * rho, qrv = qx[cb][e] * rho;
             kr[cb][e] = static_cast<_Float16>(krv);
@@ -429,9 +503,9 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
             qg[e] = static_cast<_Float16>(qrv * fb[e]);
             const float kt = kx[cb][e] * tau;
             sm.u.a.kgT[ch][tr] = static_cast<_Float16>(kt * fa[e]);
-            // column operands of column block w for row blocks i = w..3: k_s e^{G_{b_i} - G_s}
-            cv0[e] = static_cast<_Float16>(slow ? 0.f : kt * fi[e]);  // i = w (>= 1)
-            cv1[e] = static_cast<_Float16>(kt);                         // i = w + 1
+            // column operands of column block w for row blocks i = w..3: k_s e^{G_{m_i} - G_s}
+            cv0[e] = static_cast<_Float16>(slow ? 0.f : kt * fi[e]);  // i = w
+            cv1[e] = static_cast<_Float16>(kt * f1[e]);                 // i = w + 1
             cv2[e] = static_cast<_Float16>(kt * f2[e]);                 // i = w + 2
             cv3[e] = static_cast<_Float16>(kt * f3[e]);                 // i = 3 (w = 0)
         }
@@ -585,8 +659,9 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
             store_stream(reinterpret_cast<half8 *>(rec + R::PM + (tri(w, ks) * 64 + l) * 16), pf);
         }
     }
-    if (tid < K) store_stream(reinterpret_cast<float *>(rec + R::GAM) + tid, sm.fac[15][tid]);
+    if (tid < K) store_stream(reinterpret_cast<float *>(rec + R::GAM) + tid, sm.fac[18][tid]);
     raw.activate(a.gscale);  // the next item's gates
+    kqmax = raw.absmax();     // and the magnitude of its k, q
     __syncthreads();  // the next item rewrites the LDS this one read last
     }
 }
@@ -1315,10 +1390,9 @@ __global__ __launch_bounds__(64 * K / 16) void prefix_kernel(const int32_t *soff
     }
 }
 
-// pass: 0 = only the segments 0 of their sequences, 1 = only the others, 2 = all
 template <int K, int V, typename TOut, bool EPI>
 __global__ __launch_bounds__(64 * V / 16) void out_kernel(PrefillArgs a, const int32_t *off, const int32_t *soff,
-                                                          int L, const char *recs, SegBufs sb, int pass) {
+                                                          int L, const char *recs, SegBufs sb) {
     constexpr int NB = 1, NW = V / 16;
     // the fp32 epilogue tile goes into the K.e^G / Q.e^G region of a chunk buffer when it fits
     constexpr bool FTD = EPI && static_cast<size_t>(kC) * V * 4 > Rec<K>::KGT;
@@ -1329,7 +1403,6 @@ __global__ __launch_bounds__(64 * V / 16) void out_kernel(PrefillArgs a, const i
     const int s = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
     if (s >= soff[a.N]) return;
     const SegInfo si = seg_of(soff, a.N, s);
-    if ((pass == 0 && si.gl != 0) || (pass == 1 && si.gl == 0)) return;
     const int tid = threadIdx.x, l = tid & 63, r = l & 15, g = l >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col0 = 16 * NB * w;
@@ -1348,17 +1421,18 @@ __global__ __launch_bounds__(64 * V / 16) void out_kernel(PrefillArgs a, const i
     }
 }
 
-// Compute units of the current device (queried once per device).
+// Compute units of the current device, queried once per device (relaxed atomics:
+// threads that race on a first query store the same value).
 int cu_count() {
-    static int cache[64] = {0};
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cache[dev] == 0) {
-        int n = 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cache[dev] = n;
+        cache[dev].store(n, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return n;
 }
 
 // Chunks per segment: enough segments to give every compute unit a (segment,
@@ -1391,43 +1465,17 @@ struct WsLayout {
     }
 };
 
-// A second stream per device, with the events that fork it from and join it to
-// the caller's stream: the output pass of the segments 0 runs on it beside the
-// map pass, on the compute units the map pass leaves free (one workgroup per
-// middle segment and head). Created at the first prefill call on the device, at
-// default priority; calls hold the lock while they enqueue, so the fork and join
-// of concurrent callers do not interleave.
-struct SideStream {
-    hipStream_t s = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-    bool ok = false, tried = false;
-};
-std::mutex g_side_mu;
-SideStream *side_stream() {
-    static SideStream per_dev[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-    SideStream &ss = per_dev[dev];
-    if (!ss.tried) {
-        ss.tried = true;
-        ss.ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess &&
-                hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess &&
-                hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
-    }
-    return ss.ok ? &ss : nullptr;
-}
-
 template <int K, int V>
 hipError_t launch_out(const PrefillArgs &a, const int32_t *off, const int32_t *soff, int L, const char *recs,
-                      const SegBufs &sb, size_t units, int pass, hipStream_t st) {
+                      const SegBufs &sb, size_t units, hipStream_t st) {
     const dim3 og(static_cast<unsigned>(units)), ob(64 * V / 16);
     const bool epi = a.norm || a.z;
     if (a.out_dtype == KDA_BF16) {
-        if (epi) hipLaunchKernelGGL((out_kernel<K, V, bf16_t, true>), og, ob, 0, st, a, off, soff, L, recs, sb, pass);
-        else hipLaunchKernelGGL((out_kernel<K, V, bf16_t, false>), og, ob, 0, st, a, off, soff, L, recs, sb, pass);
+        if (epi) hipLaunchKernelGGL((out_kernel<K, V, bf16_t, true>), og, ob, 0, st, a, off, soff, L, recs, sb);
+        else hipLaunchKernelGGL((out_kernel<K, V, bf16_t, false>), og, ob, 0, st, a, off, soff, L, recs, sb);
     } else {
-        if (epi) hipLaunchKernelGGL((out_kernel<K, V, float, true>), og, ob, 0, st, a, off, soff, L, recs, sb, pass);
-        else hipLaunchKernelGGL((out_kernel<K, V, float, false>), og, ob, 0, st, a, off, soff, L, recs, sb, pass);
+        if (epi) hipLaunchKernelGGL((out_kernel<K, V, float, true>), og, ob, 0, st, a, off, soff, L, recs, sb);
+        else hipLaunchKernelGGL((out_kernel<K, V, float, false>), og, ob, 0, st, a, off, soff, L, recs, sb);
     }
     return hipGetLastError();
 }
@@ -1455,36 +1503,16 @@ hipError_t launch_kv(const PrefillArgs &a, hipStream_t st) {
     // every sequence has at most ceil(T / 64) chunks: one segment if that fits in L
     const int64_t maxc = (static_cast<int64_t>(a.T) + kC - 1) / kC;
     const size_t units = lay.nseg * a.H;
-    if (maxc <= lay.L) return launch_out<K, V>(a, off, soff, lay.L, recs, sb, units, 2, st);
+    if (maxc <= lay.L) return launch_out<K, V>(a, off, soff, lay.L, recs, sb, units, st);
 
     hipLaunchKernelGGL((seed_kernel<K, V>), dim3(static_cast<unsigned>(a.N) * a.H * kSeedParts), dim3(256), 0, st, a,
                        soff, sb);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    // The second stream only pays when the output pass needs more than one round
-    // of workgroups (one per compute unit): then the segments 0 start early on
-    // the units the map pass leaves free. Every sequence has a segment and the
-    // segments hold at most L chunks each, which bounds their count from below
-    // (cu_seqlens stays on the device). KDA_SIDE_STREAM=0 or 1 (read at every
-    // call) turns it off or on regardless.
-    const size_t segs = std::max<size_t>(static_cast<size_t>(a.N), (static_cast<size_t>(maxc) + lay.L - 1) / lay.L);
-    bool use_side = segs * a.H > static_cast<size_t>(cu_count());
-    if (const char *e = std::getenv("KDA_SIDE_STREAM"); e && *e) use_side = std::atoi(e) != 0;
-    SideStream *side = use_side ? side_stream() : nullptr;
-    if (side) {  // segments 0 of the output pass beside the map pass
-        if ((e = hipEventRecord(side->fork, st)) != hipSuccess) return e;
-        if ((e = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess) return e;
-        if ((e = launch_out<K, V>(a, off, soff, lay.L, recs, sb, units, 0, side->s)) != hipSuccess) return e;
-        if ((e = hipEventRecord(side->join, side->s)) != hipSuccess) return e;
-    }
     hipLaunchKernelGGL((seg_kernel<K, V>), dim3(static_cast<unsigned>(units)), dim3(64 * (K + V) / (16 * kSegNB)), 0,
                        st, a, off, soff, lay.L, recs, sb);
     if (maxc > 2 * static_cast<int64_t>(lay.L))
         hipLaunchKernelGGL((prefix_kernel<K, V>), dim3(static_cast<unsigned>(a.N) * a.H * (V / 16)), dim3(64 * K / 16), 0, st,
                            soff, a.N, a.H, sb);
-    if ((e = launch_out<K, V>(a, off, soff, lay.L, recs, sb, units, side ? 1 : 2, st)) != hipSuccess) return e;
-    if (side) e = hipStreamWaitEvent(st, side->join, 0);
-    return e;
+    return launch_out<K, V>(a, off, soff, lay.L, recs, sb, units, st);
 }
 
 }  // namespace
@@ -1497,8 +1525,6 @@ size_t prefill_mfma_workspace(int32_t N, int32_t T, int32_t H, int32_t K, int32_
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t st) {
-    const std::lock_guard<std::mutex> lock(g_side_mu);  // one enqueue sequence at a time (shared side stream)
-    side_stream();  // created at the first call, used or not, so that a later captured call creates nothing
     if (a.K == 128 && a.V == 128) return launch_kv<128, 128>(a, st);
     if (a.K == 128 && a.V == 64) return launch_kv<128, 64>(a, st);
     if (a.K == 64 && a.V == 128) return launch_kv<64, 128>(a, st);

@@ -15,8 +15,10 @@
 // into the token recurrence gives (I + A) U' = Diag(beta)(V - (K.e^G) S),
 // hence these lines exactly.
 //
-// Every quantity is fp32; the pairwise decays are evaluated element by
-// element (one exp per (r, s, channel)), so no factorisation can overflow.
+// Every quantity is fp32. The pairwise decays are the products
+// e^{G_r} e^{-G_s} (one exp per token and channel) while the chunk decays by
+// less than e^80 in every channel, so neither factor leaves the normal fp32
+// range; a chunk that decays further evaluates e^{G_r - G_s} element by element.
 // Rows past the end of a partial chunk are zero-filled with g = 0 and
 // beta = 0, which makes them contribute nothing.
 //

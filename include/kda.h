@@ -25,18 +25,8 @@
  * Conventions shared by every entry point
  *  - Every pointer argument is DEVICE memory on the current HIP device,
  *    owned by the caller. The library never allocates or frees device memory
- *    and never synchronises; the work runs asynchronously, ordered on `stream`.
- *    The prefill entry points may run part of a call on a second stream of
- *    the library's own (one per device, created with two events at the first
- *    call that needs it, default priority, kept until the process ends),
- *    forked from and joined back to `stream` with those events: the call as a
- *    whole is still ordered on `stream`, and can be captured in a HIP graph
- *    (the first prefill call on a device, which creates the stream, should
- *    then come before the capture). By default the second stream is used when
- *    the call has more state-pass segments than the device has compute units;
- *    KDA_SIDE_STREAM=0 or 1 in the environment (read at every call) keeps all
- *    work on `stream`, or uses the second stream whenever a sequence spans
- *    several segments.
+ *    and never synchronises; all of a call's work is enqueued on `stream`, in
+ *    order, so a call can be captured in a HIP graph.
  *  - Every pointer must be 16-byte aligned; tensors are dense, row-major,
  *    with the layouts given below (last dimension contiguous).
  *  - Arguments are validated on the host before anything is enqueued. A
@@ -48,15 +38,25 @@
  *  - Device-side contents are the caller's contract and are not checked:
  *    cu_seqlens must be non-decreasing from 0 to T_total, log_alpha finite
  *    and <= 0, slot indices distinct and in range. Stability of the
- *    recurrence needs ||k_t|| <= 1 and beta_t in [0, 2].
+ *    recurrence needs beta_t ||k_t||^2 in [0, 2] (e.g. ||k_t|| <= 1 and
+ *    beta_t in [0, 2]).
+ *  - bf16 prefill: its pairwise key/query products run on fp16 operands, so
+ *    every q and k component must be below 6.5e4 in magnitude. A chunk in
+ *    which some 16-token sub-chunk decays by more than e^10 in a channel, or
+ *    in which a q or k component times the decay over half a sub-chunk could
+ *    pass 3e4, evaluates its diagonal 16 x 16 blocks element by element in
+ *    fp32 instead (slower, same result); v, the states and the outputs have
+ *    no such bound (they are scaled by powers of two before every fp16
+ *    conversion).
  *  - Test overrides, read from the environment: KDA_SEG_CHUNKS=n (at every
  *    call) cuts the state passes of the bf16 prefill into segments of n
  *    chunks (at most the chunk count), and KDA_PREFILL_KERNEL=valu (once per
  *    process) runs bf16 inputs through the fp32 prefill kernels. The workspace
  *    size depends on both: query it under the environment of the call.
- *  - Apart from that stream and its events, the library holds no global
- *    mutable state. Calls are thread-safe (prefill calls take a lock while
- *    they enqueue); calls on different streams that write the same memory race.
+ *  - The library's only global state is a per-device cache of the compute
+ *    unit count (atomic). Calls are thread-safe and take no lock; calls on
+ *    different streams that write the same memory (outputs, states, a shared
+ *    workspace) race.
  *  - No C++ exception crosses this interface.
  */
 #ifndef KDA_H_

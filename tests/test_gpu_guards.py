@@ -57,11 +57,10 @@ def _prefill(d, dt, ex=None):
     assert torch.equal(o.t, ro) and torch.equal(fin.t, rs)
 
 
-@pytest.mark.parametrize("seg,side", [(None, None), ("2", "1"), ("3", "0")])
-def test_prefill_bf16_writes_nothing_outside(seg, side, monkeypatch):
+@pytest.mark.parametrize("seg", [None, "2", "3"])
+def test_prefill_bf16_writes_nothing_outside(seg, monkeypatch):
     if seg is not None:
         monkeypatch.setenv("KDA_SEG_CHUNKS", seg)
-        monkeypatch.setenv("KDA_SIDE_STREAM", side)
     d = gc.to_device(inputs.prefill_inputs(41, [300, 0, 77, 1, 200], 3, 128, 128, "bf16", 0.1, "random"))
     _prefill(d, "bf16")
 

@@ -79,18 +79,17 @@ def test_decode_steps_equal_prefill(dt):
     gc.assert_close("state (decode vs prefill)", gc.host(state), gc.host(sT).astype(np.float64), tol)
 
 
-@pytest.mark.parametrize("name,seg,side,reps,epi", [
-    ("long_128k", None, None, 6, False),
-    ("mid_4x4k", "2", "1", 16, False),
-    ("mid_4x4k", "3", "0", 16, False),
-    ("mid_4x4k", "2", "1", 8, True),
+@pytest.mark.parametrize("name,seg,reps,epi", [
+    ("long_128k", None, 6, False),
+    ("mid_4x4k", "2", 16, False),
+    ("mid_4x4k", "3", 16, False),
+    ("mid_4x4k", "2", 8, True),
 ])
-def test_repeated_calls_are_bitwise_identical(name, seg, side, reps, epi, monkeypatch):
-    for key, val in (("KDA_SEG_CHUNKS", seg), ("KDA_SIDE_STREAM", side)):
-        if val is None:
-            monkeypatch.delenv(key, raising=False)
-        else:
-            monkeypatch.setenv(key, val)
+def test_repeated_calls_are_bitwise_identical(name, seg, reps, epi, monkeypatch):
+    if seg is None:
+        monkeypatch.delenv("KDA_SEG_CHUNKS", raising=False)
+    else:
+        monkeypatch.setenv("KDA_SEG_CHUNKS", seg)
     d = inputs.device_workload_inputs(name)
     ex = {}
     if epi:

@@ -99,15 +99,14 @@ def test_output_epilogue(dt, norm, z_act):
 
 @pytest.mark.parametrize("case", [
     dict(seed=7051, lens=[129, 129, 2, 128, 129, 127], Hk=3, H=6, K=64, V=128, z_act=None,
-         slots=[3, -1, 8, 5, 4, 6], seg="1", side="1"),
-    dict(seed=7114, lens=[1, 129], Hk=1, H=3, K=128, V=64, z_act="none", slots=[-1, 1], seg="3", side="0"),
+         slots=[3, -1, 8, 5, 4, 6], seg="1"),
+    dict(seed=7114, lens=[1, 129], Hk=1, H=3, K=128, V=64, z_act="none", slots=[-1, 1], seg="3"),
 ])
 def test_output_norm_strong_decay(case, monkeypatch):
     """Strong decay (log alpha = -0.5 softplus(x)) and the RMS norm: rows whose
     output is small before the norm (here down to 7 % of RMS(o)) are scaled up
     by it, and their error with them, so o is held to the propagated bound."""
     monkeypatch.setenv("KDA_SEG_CHUNKS", case["seg"])
-    monkeypatch.setenv("KDA_SIDE_STREAM", case["side"])
     _prefill_case(case["seed"], case["lens"], case["Hk"], case["H"], case["K"], case["V"], "bf16", gates="pre",
                   norm=True, z_act=case["z_act"], slots=case["slots"], decay=0.5)
 
@@ -116,7 +115,6 @@ def test_output_norm_strong_decay(case, monkeypatch):
 @pytest.mark.parametrize("seg", ["2", "16"])
 def test_state_slots(dt, seg, monkeypatch):
     monkeypatch.setenv("KDA_SEG_CHUNKS", seg)
-    monkeypatch.setenv("KDA_SIDE_STREAM", "1")
     # shuffled slots, a padding sequence and an empty one; several segments per sequence
     _prefill_case(24, [300, 0, 77, 260], 2, 2, 128, 128, dt, gates="plain", slots=[5, 2, -1, 0])
 
@@ -131,7 +129,6 @@ def test_no_tokens_with_slots_and_epilogue(dt):
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64), (64, 64)])
 def test_all_options_together(dk, dv, monkeypatch):
     monkeypatch.setenv("KDA_SEG_CHUNKS", "2")
-    monkeypatch.setenv("KDA_SIDE_STREAM", "1")
     _prefill_case(25, [333, 5, 180], 2, 4, dk, dv, "bf16", gates="pre", norm=True, z_act="sigmoid",
                   slots=[1, 3, 0])
 
@@ -224,15 +221,12 @@ def test_decode_steps_replayed_from_a_hip_graph_match_eager():
         _ = (state * 2).sum().item()   # eager work between replays
 
 
-@pytest.mark.parametrize("side", ["0", "1"])
-def test_prefill_replayed_from_a_hip_graph_matches_eager(side, monkeypatch):
+def test_prefill_replayed_from_a_hip_graph_matches_eager(monkeypatch):
     """Prefill (plain and extended, several segments per sequence, so every kernel
-    of the call runs; with side = 1 the first segments on the library's second
-    stream) captured once in a HIP graph with caller-provided outputs and
+    of the call runs) captured once in a HIP graph with caller-provided outputs and
     workspace, replayed three times with eager work and synchronisation between
     the replays: outputs and final states equal the eager ones bitwise."""
     monkeypatch.setenv("KDA_SEG_CHUNKS", "2")
-    monkeypatch.setenv("KDA_SIDE_STREAM", side)
     lens = [300, 77, 500]
     Hk, H, K, V = 2, 4, 128, 128
     T, N = sum(lens), len(lens)

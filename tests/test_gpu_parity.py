@@ -80,6 +80,29 @@ def test_prefill_strong_decay(dt, decay):
     _prefill_case(inputs.prefill_inputs(9, [300], 2, 128, 128, dt, decay, "random"))
 
 
+@pytest.mark.parametrize("spike", [False, True])
+def test_prefill_unnormalised_keys(spike):
+    """Stable but unnormalised keys: ||k|| = 4 with beta <= 0.12 (beta ||k||^2 <=
+    1.92), every 16-token sub-chunk decaying by e^9.84 in every channel. With a spike
+    (one channel of each key near 3.5) the diagonal column operand k_s e^{G_b - G_s}
+    of the fp16 path would pass the fp16 maximum, so those chunks take the exact
+    fp32 diagonal path; without it the components stay near 1 and the fp16 path runs
+    with operands up to about 2.5e4."""
+    seed = 31 + int(spike)
+    rng = np.random.default_rng(seed)
+    inp = inputs.prefill_inputs(seed, [300, 77], 2, 128, 128, "bf16", 0.1, "random", rng=rng)
+    T, H, K = inp.k.shape
+    k = rng.standard_normal((T, H, K)).astype(np.float32)
+    if spike:
+        k *= 0.05
+        np.put_along_axis(k, rng.integers(0, K, size=(T, H, 1)), 1.0, axis=2)
+    inp.k = inputs.bf16_round(4.0 * k / np.linalg.norm(k, axis=2, keepdims=True))
+    assert (np.abs(inp.k).max() > 3.3) == spike
+    inp.beta = (np.float32(0.12) * inp.beta).astype(np.float32)
+    inp.log_alpha = np.full_like(inp.log_alpha, -0.615)
+    _prefill_case(inp)
+
+
 def test_prefill_null_vs_zero_state_alias_and_determinism():
     inp = inputs.prefill_inputs(10, [100, 200], 4, 128, 128, "bf16", 0.1, "zero")
     d = gc.to_device(inp)
@@ -101,13 +124,11 @@ def test_prefill_null_vs_zero_state_alias_and_determinism():
 
 @pytest.mark.parametrize("seg", ["1", "2", "3", "2147483647"])
 def test_prefill_segmented_state_pass(seg, monkeypatch):
-    """The state pass cut into segments of `seg` chunks (map pass with the first
-    segments' output pass beside it on the second stream, prefix over segments,
-    output pass) on ragged packed sequences, including empty ones, with a random
+    """The state pass cut into segments of `seg` chunks (map pass, prefix over
+    segments, output pass) on ragged packed sequences, including empty ones, with a random
     initial state; final_state aliasing initial_state. The largest override is
     cut to the chunk count (one segment per sequence)."""
     monkeypatch.setenv("KDA_SEG_CHUNKS", seg)
-    monkeypatch.setenv("KDA_SIDE_STREAM", "1")
     inp = inputs.prefill_inputs(11, [0, 700, 64, 1, 389, 0, 200], 3, 128, 128, "bf16", 0.1, "random")
     d = _prefill_case(inp)
     o1, s1 = gc.run_prefill(d)
@@ -121,7 +142,6 @@ def test_prefill_segmented_state_pass(seg, monkeypatch):
 @pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64), (64, 64)])
 def test_prefill_segmented_head_dims(dk, dv, monkeypatch):
     monkeypatch.setenv("KDA_SEG_CHUNKS", "2")
-    monkeypatch.setenv("KDA_SIDE_STREAM", "1")
     _prefill_case(inputs.prefill_inputs(12, [520, 70, 300], 2, dk, dv, "bf16", 0.1, "random"))
 
 

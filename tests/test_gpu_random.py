@@ -2,8 +2,7 @@
 and lengths (empty, single-token, partial and several chunks), key-head
 grouping, head sizes, input type, gate form, output epilogue, slot caches and
 segment length (so that the map pass, the prefix and the output pass all take
-part; odd cases run the first segments on the second stream), each against the
-fp64 oracle with the same options."""
+part), each against the fp64 oracle with the same options."""
 
 import numpy as np
 import pytest
@@ -43,7 +42,6 @@ def test_random_configuration(i, monkeypatch):
     print(f"  case {i}: {c}", flush=True)
     if c["seg"] is not None:
         monkeypatch.setenv("KDA_SEG_CHUNKS", c["seg"])
-    monkeypatch.setenv("KDA_SIDE_STREAM", str(i % 2))
     _prefill_case(2000 + i, c["lens"], c["Hk"], c["H"], c["K"], c["V"], c["dt"], gates=c["gates"], norm=c["norm"],
                   z_act=c["z_act"], slots=c["slots"])
 
@@ -73,7 +71,6 @@ def test_random_large_configuration(i, monkeypatch):
     own segment length and choice of streams."""
     import torch
     monkeypatch.delenv("KDA_SEG_CHUNKS", raising=False)
-    monkeypatch.delenv("KDA_SIDE_STREAM", raising=False)
     c = _large_config(i)
     print(f"  large case {i}: T={sum(c['lens'])} {c}", flush=True)
     _prefill_case(8000 + i, c["lens"], c["Hk"], c["H"], c["K"], c["V"], "bf16", gates=c["gates"], norm=c["norm"],
