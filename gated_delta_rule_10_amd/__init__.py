@@ -5,8 +5,8 @@ include/kda.h); `gated_delta_rule_10_amd.kda` is its Python binding and
 `gated_delta_rule_10_amd.inputs` draws seeded synthetic inputs.
 """
 
-__all__ = ["kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_workspace_size",
-           "kda_abi_version", "kda_status_string", "KDAError"]
+__all__ = ["kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd_ex",
+           "kda_decode_step_ex", "kda_chunk_fwd_ex_noalloc", "kda_abi_version", "kda_status_string", "KDAError"]
 
 
 def __getattr__(name):

@@ -84,7 +84,7 @@ kda_status_t chunk_fwd(const void *q, const void *k, const void *v, const float 
                        const int32_t *cu_seqlens, int32_t N, int32_t T_total, int32_t H, int32_t d_k, int32_t d_v,
                        kda_dtype_t in_dtype, kda_dtype_t out_dtype, float scale, const float *initial_state,
                        float *final_state, void *o, int32_t chunk_size, void *workspace, size_t workspace_bytes,
-                       const kda_options_t *opt, hipStream_t stream) {
+                       const kda_options_t *opt, hipStream_t stream, bool noalloc = false) {
     if (N < 1 || H < 1 || T_total < 0) return KDA_ERR_INVALID_ARG;
     if (!dtype_valid(in_dtype) || !dtype_valid(out_dtype)) return KDA_ERR_INVALID_ARG;
     if (!cu_seqlens || !aligned16(cu_seqlens)) return KDA_ERR_INVALID_ARG;
@@ -107,6 +107,12 @@ kda_status_t chunk_fwd(const void *q, const void *k, const void *v, const float 
     if (static_cast<int64_t>(T_total) * H * (d_k > d_v ? d_k : d_v) > (int64_t(1) << 40))
         return KDA_ERR_INVALID_ARG;
     const size_t need = kda_chunk_fwd_workspace_size(N, T_total, H, d_k, d_v, in_dtype);
+    if (noalloc) {  // the library's static scratch, once every argument has passed
+        if (need > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE;
+        workspace = nullptr;
+        workspace_bytes = need;
+        if (need > 0 && !(workspace = kda::noalloc_scratch())) return KDA_ERR_HIP;
+    }
     if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
 
     kda::PrefillArgs a{};
@@ -204,6 +210,16 @@ kda_status_t kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const
                               size_t workspace_bytes, const kda_options_t *opt, hipStream_t stream) {
     return chunk_fwd(q, k, v, log_alpha, beta, cu_seqlens, N, T_total, H, d_k, d_v, in_dtype, out_dtype, scale,
                      initial_state, final_state, o, chunk_size, workspace, workspace_bytes, opt, stream);
+}
+
+kda_status_t kda_chunk_fwd_ex_noalloc(const void *q, const void *k, const void *v, const float *log_alpha,
+                                      const float *beta, const int32_t *cu_seqlens, int32_t N, int32_t T_total,
+                                      int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t in_dtype,
+                                      kda_dtype_t out_dtype, float scale, const float *initial_state,
+                                      float *final_state, void *o, int32_t chunk_size, const kda_options_t *opt,
+                                      hipStream_t stream) {
+    return chunk_fwd(q, k, v, log_alpha, beta, cu_seqlens, N, T_total, H, d_k, d_v, in_dtype, out_dtype, scale,
+                     initial_state, final_state, o, chunk_size, nullptr, 0, opt, stream, true);
 }
 
 kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,

@@ -70,4 +70,9 @@ size_t prefill_mfma_workspace(int32_t N, int32_t T, int32_t H, int32_t K, int32_
 // workspace of the fp32 vector-ALU path: one fp32 record per (chunk slot, head)
 size_t prefill_valu_workspace(int32_t N, int32_t T, int32_t H, int32_t K);
 
+// Device address of the current device's copy of the static scratch of
+// kda_chunk_fwd_ex_noalloc (KDA_NOALLOC_SCRATCH_BYTES), looked up once per
+// device; nullptr if the lookup fails.
+void *noalloc_scratch();
+
 }  // namespace kda

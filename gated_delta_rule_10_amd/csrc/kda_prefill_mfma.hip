@@ -1515,7 +1515,25 @@ hipError_t launch_kv(const PrefillArgs &a, hipStream_t st) {
     return launch_out<K, V>(a, off, soff, lay.L, recs, sb, units, st);
 }
 
+// Workspace of kda_chunk_fwd_ex_noalloc. In host code this name is the runtime's
+// stand-in for the device array, not a device address: only the address from
+// hipGetSymbolAddress (taken per device, below) goes to kernels.
+static __device__ __align__(256) char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
 }  // namespace
+
+void *noalloc_scratch() {
+    static std::atomic<void *> addr[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    void *p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        // with `dev` current: each GPU holds its own copy of the array at its own address
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        addr[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
 
 size_t prefill_mfma_workspace(int32_t N, int32_t T, int32_t H, int32_t K, int32_t V) {
     if (K == 128 && V == 128) return WsLayout<128, 128>(N, T, H).bytes;

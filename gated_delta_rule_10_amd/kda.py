@@ -71,6 +71,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_chunk_fwd_ex.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, ctypes.c_int,
                                      ctypes.c_int, f32, P, P, P, i32, P, sz, opt, P]
     lib.kda_chunk_fwd_ex.restype = ctypes.c_int
+    lib.kda_chunk_fwd_ex_noalloc.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, ctypes.c_int,
+                                             ctypes.c_int, f32, P, P, P, i32, opt, P]
+    lib.kda_chunk_fwd_ex_noalloc.restype = ctypes.c_int
     lib.kda_decode_step_ex.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
                                        ctypes.c_int, ctypes.c_int, f32, opt, P]
     lib.kda_decode_step_ex.restype = ctypes.c_int
@@ -269,17 +272,32 @@ def _options(H, num_k_heads=None, gate_x=None, beta_y=None, gate_scale=1.0, norm
 
 
 def kda_chunk_fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor, *,
-                     log_alpha: Optional[torch.Tensor] = None, beta: Optional[torch.Tensor] = None,
-                     gate_x: Optional[torch.Tensor] = None, beta_y: Optional[torch.Tensor] = None,
-                     gate_scale: float = 1.0, norm: bool = False, norm_eps: float = 1e-6,
-                     norm_weight: Optional[torch.Tensor] = None, out_gate: Optional[torch.Tensor] = None,
-                     out_gate_act="none", state_slots: Optional[torch.Tensor] = None,
-                     scale: float = 1.0, initial_state: Optional[torch.Tensor] = None,
-                     output_final_state: bool = True, final_state: Optional[torch.Tensor] = None,
-                     out_dtype: Optional[torch.dtype] = None, o: Optional[torch.Tensor] = None,
-                     workspace: Optional[torch.Tensor] = None,
-                     stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """kda_chunk_fwd_ex of include/kda.h.
+                     workspace: Optional[torch.Tensor] = None, **kw) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """kda_chunk_fwd_ex of include/kda.h (arguments as for _chunk_fwd_ex below; the
+    workspace is the caller's or, when None, a new one of the size the library asks for)."""
+    return _chunk_fwd_ex(q, k, v, cu_seqlens, noalloc=False, workspace=workspace, **kw)
+
+
+def kda_chunk_fwd_ex_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                             **kw) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """kda_chunk_fwd_ex_noalloc of include/kda.h: no workspace; the library works in its
+    static scratch. Pass o (and final_state, or output_final_state=False) to have the
+    binding allocate nothing either."""
+    return _chunk_fwd_ex(q, k, v, cu_seqlens, noalloc=True, workspace=None, **kw)
+
+
+def _chunk_fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor, *,
+                  noalloc: bool, log_alpha: Optional[torch.Tensor] = None, beta: Optional[torch.Tensor] = None,
+                  gate_x: Optional[torch.Tensor] = None, beta_y: Optional[torch.Tensor] = None,
+                  gate_scale: float = 1.0, norm: bool = False, norm_eps: float = 1e-6,
+                  norm_weight: Optional[torch.Tensor] = None, out_gate: Optional[torch.Tensor] = None,
+                  out_gate_act="none", state_slots: Optional[torch.Tensor] = None,
+                  scale: float = 1.0, initial_state: Optional[torch.Tensor] = None,
+                  output_final_state: bool = True, final_state: Optional[torch.Tensor] = None,
+                  out_dtype: Optional[torch.dtype] = None, o: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None,
+                  stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """kda_chunk_fwd_ex (noalloc: kda_chunk_fwd_ex_noalloc) of include/kda.h.
 
     q, k: [T, Hk, d_k]; v: [T, H, d_v] with H a multiple of Hk (value head h uses key
     head h // (H // Hk)); gates either log_alpha [T, H, d_k] fp32 and beta [T, H] fp32,
@@ -333,6 +351,18 @@ def kda_chunk_fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqle
                 raise ValueError(f"{name} must be float32 [{'slots' if state_slots is not None else 'N'}, H, d_k, d_v]")
     op = _options(H, Hk, gate_x, beta_y, gate_scale, norm, norm_eps, norm_weight, out_gate, out_gate_act,
                   state_slots, num_slots)
+    if noalloc:
+        _one_device(q.device, k, v, cu_seqlens, log_alpha, beta, gate_x, beta_y, norm_weight, out_gate,
+                    state_slots, initial_state, final_state, o)
+        with torch.cuda.device(q.device):
+            st = lib.kda_chunk_fwd_ex_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                              _ptr(cu_seqlens), N, T, H, d_k, d_v, _code(q.dtype),
+                                              _code(out_dtype), float(scale), _ptr(initial_state),
+                                              _ptr(final_state), _ptr(o), CHUNK_SIZE, ctypes.byref(op),
+                                              _stream(stream, q.device))
+        if st != KDA_OK:
+            raise KDAError(st, "kda_chunk_fwd_ex_noalloc")
+        return o, final_state
     workspace, ws_bytes = _workspace(lib, workspace, N, T, H, d_k, d_v, q.dtype, q.device)
     _one_device(q.device, k, v, cu_seqlens, log_alpha, beta, gate_x, beta_y, norm_weight, out_gate, state_slots,
                 initial_state, final_state, o, workspace)

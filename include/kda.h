@@ -257,6 +257,40 @@ kda_status_t kda_decode_step_ex(const void *q, const void *k, const void *v,
                                 float scale, const kda_options_t *opt,
                                 hipStream_t stream);
 
+/*
+ * Bytes of the library's static scratch, the workspace of
+ * kda_chunk_fwd_ex_noalloc: one array per GPU in the library's code object,
+ * held from the first use of the library on that GPU until the process ends.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+/*
+ * kda_chunk_fwd_ex without the workspace arguments, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. The call allocates nothing and calls no
+ * allocating routine; its workspace is the library's static scratch of the
+ * current device (KDA_NOALLOC_SCRATCH_BYTES).
+ *  - Returns KDA_ERR_WORKSPACE, with nothing enqueued, when
+ *    kda_chunk_fwd_workspace_size(N, T_total, H, d_k, d_v, in_dtype) exceeds
+ *    KDA_NOALLOC_SCRATCH_BYTES (e.g. a 4,096-token bf16 call at H = 32 and
+ *    d = 128 fits, and one 16 times larger does not); KDA_ERR_HIP if the
+ *    scratch's address cannot be obtained. Every other argument and error is
+ *    as for kda_chunk_fwd_ex.
+ *  - Every call on a GPU uses that GPU's one scratch array, which keeps the
+ *    previous call's contents (no call needs it cleared: each writes what it
+ *    reads). Calls that overlap on one GPU (different streams, or host
+ *    threads, without ordering between them) race on it and must not be made.
+ */
+kda_status_t kda_chunk_fwd_ex_noalloc(const void *q, const void *k, const void *v,
+                                      const float *log_alpha, const float *beta,
+                                      const int32_t *cu_seqlens, int32_t N,
+                                      int32_t T_total, int32_t H, int32_t d_k,
+                                      int32_t d_v, kda_dtype_t in_dtype,
+                                      kda_dtype_t out_dtype, float scale,
+                                      const float *initial_state, float *final_state,
+                                      void *o, int32_t chunk_size,
+                                      const kda_options_t *opt, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,7 +32,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_size",
-        "kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_ex", "kda_decode_step_ex"])
+        "kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_ex", "kda_decode_step_ex",
+        "kda_chunk_fwd_ex_noalloc"])
 
 
 def test_options_struct_layout_matches_the_header(tmp_path):
@@ -211,3 +212,25 @@ def test_binding_helpers_refuse_mixed_devices_and_wrong_outputs():
         kb._out(torch.empty((4, 2, 7), dtype=torch.bfloat16), (4, 2, 8), torch.bfloat16, dev)
     with pytest.raises(ValueError, match="o must be"):
         kb._out(torch.empty((4, 2, 8), dtype=torch.float32), (4, 2, 8), torch.bfloat16, dev)
+
+
+def test_noalloc_rejects_on_the_host(lib):
+    """kda_chunk_fwd_ex_noalloc: a call whose workspace would pass the static scratch
+    is refused with KDA_ERR_WORKSPACE before any HIP call (this host has no GPU), and
+    invalid arguments are refused as by kda_chunk_fwd_ex."""
+    def call(**over):
+        a = dict(q=A, k=A, v=A, g=A, b=A, cu=A, N=1, T=1 << 20, H=32, dk=128, dv=128,
+                 din=kda.KDA_BF16, dout=kda.KDA_BF16, chunk=64)
+        a.update(over)
+        return lib.kda_chunk_fwd_ex_noalloc(a["q"], a["k"], a["v"], a["g"], a["b"], a["cu"], a["N"], a["T"],
+                                            a["H"], a["dk"], a["dv"], a["din"], a["dout"], 1.0, None, None,
+                                            a["q"], a["chunk"], None, None)
+    import torch
+    limit = 256 << 20
+    assert kda.kda_chunk_fwd_workspace_size(1, 1 << 20, 32, 128, 128, torch.bfloat16) > limit
+    assert call() == kda.KDA_ERR_WORKSPACE
+    assert kda.kda_chunk_fwd_workspace_size(1, 4096, 32, 128, 128, torch.bfloat16) <= limit
+    assert call(T=65536) == kda.KDA_ERR_WORKSPACE
+    assert call(N=0, T=4096) == kda.KDA_ERR_INVALID_ARG
+    assert call(T=4096, dk=96) == kda.KDA_ERR_UNSUPPORTED
+    assert call(T=4096, chunk=32) == kda.KDA_ERR_UNSUPPORTED
