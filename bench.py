@@ -369,28 +369,41 @@ def main():
             result["variants"][wname] = time_prefill_workload(wname, wsteps, wwarm, dev, stream)
 
     # ---- decode: 64 sequences x 32 heads, fp32 cache -----------------------
+    # The figure of record reads the state from HBM: four independent 128 MiB
+    # caches are cycled step by step (512 MiB, twice the 256 MB Infinity Cache),
+    # so the state a step reads was last touched three steps (800 MB of traffic)
+    # earlier, as it is in a model whose every layer keeps its own cache. The
+    # steps on one cache, which can stay in the Infinity Cache, are a variant.
     if not args.prefill_only:
         steps = args.decode_steps
         dd = inputs.device_workload_inputs("decode_b64", device=dev, steps=steps)
         Bd, Hd, Kd, Vd = 64, 32, 128, 128
         state = dd["state"]
         od = torch.empty((Bd, Hd, Vd), dtype=torch.bfloat16, device=dev)
+        dbytes = decode_bytes(Bd, Hd, Kd, Vd)
+        NCACHE = 4
+        caches = [state] + [state.clone() for _ in range(NCACHE - 1)]
 
-        def dstep(s):
-            kda.kda_decode_step(dd["q"][s], dd["k"][s], dd["v"][s], dd["log_alpha"][s],
-                                dd["beta"][s], state, o=od, stream=stream)
+        def dsteps(cache_of, n0, n):
+            for s in range(n0, n0 + n):
+                kda.kda_decode_step(dd["q"][s % steps], dd["k"][s % steps], dd["v"][s % steps],
+                                    dd["log_alpha"][s % steps], dd["beta"][s % steps], cache_of(s), o=od,
+                                    stream=stream)
 
-        for s in range(min(args.warmup, steps)):
-            dstep(s)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for s in range(steps):
-            dstep(s)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / steps
-        # the plain steps from a captured HIP graph as well
+        def timed(cache_of):
+            dsteps(cache_of, 0, min(args.warmup, steps) + NCACHE)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dsteps(cache_of, 0, steps)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / steps
+
+        us = timed(lambda s: caches[s % NCACHE])
+        warm_us = timed(lambda s: state)
+        del caches
+        # the one-cache steps from a captured HIP graph as well
         Gp = min(steps, 64)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -407,17 +420,22 @@ def main():
                                     state, o=od)
         graph_us = time_calls(pgraph.replay, max(1, steps // Gp), 1, stream) * 1e3 / Gp
         del pgraph
-        dbytes = decode_bytes(Bd, Hd, Kd, Vd)
         dgbs = dbytes / (us / 1e6) / 1e9
+        wgbs = dbytes / (warm_us / 1e6) / 1e9
         result["decode"] = {
             "value": round(us, 3), "unit": "us/step", "steps": steps,
-            "workload": "decode_b64: B=64, H=32, d_k=d_v=128, fp32 state cache (128 MiB), "
-                        "bf16 q/k/v/o, fresh inputs every step",
-            "graph_us_per_step": round(graph_us, 3),
+            "workload": "decode_b64: B=64, H=32, d_k=d_v=128, fp32 state cache (128 MiB), bf16 q/k/v/o, "
+                        "fresh inputs every step; four caches cycled step by step (512 MiB), so the "
+                        "state comes from HBM",
             "roofline": {"bound": "hbm", "achieved": round(dgbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(dgbs / PEAK_HBM_GBS, 4),
                          "traffic": measured_traffic("decode_b64.md"),
                          "algorithmic_bytes_per_launch": dbytes},
+            "variants": {"mall_resident": {
+                "entry": "kda_decode_step, one 128 MiB cache every step (it fits the 256 MB Infinity Cache)",
+                "value": round(warm_us, 3), "unit": "us/step", "graph_us_per_step": round(graph_us, 3),
+                "achieved_gbs": round(wgbs, 1),
+                "note": "not an HBM figure: part of the state may come from the Infinity Cache"}},
         }
         if not args.no_variants:
             gen = torch.Generator(device=dev)
@@ -454,35 +472,11 @@ def main():
                     dfused()
             reps = max(1, steps // G)
             gus = time_calls(graph.replay, reps, 1, stream) * 1e3 / G
-            result["decode"]["variants"] = {"fused_gates_norm_gate": {
-                "entry": "kda_decode_step_ex (gate_x, beta_y bf16; norm + weight; sigmoid output gate)",
+            result["decode"]["variants"]["fused_gates_norm_gate"] = {
+                "entry": "kda_decode_step_ex (gate_x, beta_y bf16; norm + weight; sigmoid output gate), one cache",
                 "value": round(gus, 3), "unit": "us/step", "timing": f"HIP graph of {G} steps, {reps} replays",
-                "eager_us_per_step": round(dus, 3)}}
+                "eager_us_per_step": round(dus, 3)}
             del graph
-
-            # The 128 MiB cache fits in the 256 MB Infinity Cache, so the steps above may
-            # read part of the state from there. Here four independent caches are cycled
-            # (512 MiB): the state a step reads was last touched three steps (800 MB of
-            # traffic) earlier, so it comes from HBM.
-            NCACHE = 4
-            caches = [state.clone() for _ in range(NCACHE)]
-            ci = [0]
-
-            def dcold():
-                c = ci[0] % NCACHE
-                s = ci[0] % steps
-                ci[0] += 1
-                kda.kda_decode_step(dd["q"][s], dd["k"][s], dd["v"][s], dd["log_alpha"][s], dd["beta"][s],
-                                    caches[c], o=od, stream=stream)
-
-            cus = time_calls(dcold, steps, min(args.warmup, steps) + NCACHE, stream) * 1e3
-            cgbs = dbytes / (cus / 1e6) / 1e9
-            result["decode"]["variants"]["cache_defeating"] = {
-                "entry": "kda_decode_step, 4 state caches cycled step by step (512 MiB working set)",
-                "value": round(cus, 3), "unit": "us/step",
-                "roofline": {"bound": "hbm", "achieved": round(cgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                             "frac": round(cgbs / PEAK_HBM_GBS, 4), "algorithmic_bytes_per_launch": dbytes}}
-            del caches
         if cpu_d is not None:
             result["decode"]["cpu_baseline"] = cpu_baseline_decode(dd)
         del dd, state
