@@ -147,29 +147,57 @@ def test_prefill_segmented_head_dims(dk, dv, monkeypatch):
 
 def test_prefill_long_128k_sampled():
     """One 131072-token sequence, H=32, d=128, bf16, random initial state:
-    heads 0 and 31 computed completely by the oracle."""
+    heads 0 and 31 computed completely by the oracle, for bf16 outputs and for
+    fp32 outputs (the error before the final bf16 rounding, held to the bar
+    directly)."""
     d = inputs.device_workload_inputs("long_128k")
-    o, sT = gc.run_prefill(d)
     heads = [0, 31]
     ref_o, ref_s, _ = gc.oracle_prefill(d, heads=heads)
     hd = torch.tensor(heads, device="cuda")
-    gc.assert_close("o", gc.host(o.index_select(1, hd)), ref_o, gc.TOL_BF16, bf16_rounded=True)
-    gc.assert_close("final_state", gc.host(sT.index_select(1, hd)), ref_s, gc.TOL_BF16)
+    for od in (torch.bfloat16, torch.float32):
+        o, sT = gc.run_prefill(d, out_dtype=od)
+        gc.assert_close(f"o[{od}]", gc.host(o.index_select(1, hd)), ref_o, gc.TOL_BF16,
+                        bf16_rounded=od == torch.bfloat16)
+        gc.assert_close("final_state", gc.host(sT.index_select(1, hd)), ref_s, gc.TOL_BF16)
 
 
 def test_prefill_varlen_512k_sampled():
     """16 packed sequences, 524288 tokens, H=32: the shortest and the longest
-    sequence on two heads computed completely by the oracle."""
+    sequence on all 32 heads computed completely by the oracle (bf16 outputs),
+    and two of those heads again with fp32 outputs."""
     d = inputs.device_workload_inputs("varlen_512k")
-    o, sT = gc.run_prefill(d)
     cu = d["cu_seqlens"].cpu().numpy()
     lens = np.diff(cu)
     seqs = [int(np.argmin(lens)), int(np.argmax(lens))]
+    ref_o, ref_s, tok = gc.oracle_prefill(d, seqs=seqs)
+    tk = torch.from_numpy(tok).cuda()
+    sq = torch.tensor(seqs, device="cuda")
+    o, sT = gc.run_prefill(d)
+    gc.assert_close("o (all heads)", gc.host(o.index_select(0, tk)), ref_o, gc.TOL_BF16, bf16_rounded=True)
+    gc.assert_close("final_state (all heads)", gc.host(sT.index_select(0, sq)), ref_s, gc.TOL_BF16)
     heads = [3, 17]
-    ref_o, ref_s, tok = gc.oracle_prefill(d, heads=heads, seqs=seqs)
     hd = torch.tensor(heads, device="cuda")
-    got_o = gc.host(o.index_select(0, torch.from_numpy(tok).cuda()).index_select(1, hd))
-    got_s = gc.host(sT.index_select(0, torch.tensor(seqs, device="cuda")).index_select(1, hd))
+    o, sT = gc.run_prefill(d, out_dtype=torch.float32)
+    gc.assert_close("o[fp32] (heads 3, 17)", gc.host(o.index_select(0, tk).index_select(1, hd)), ref_o[:, heads],
+                    gc.TOL_BF16)
+    gc.assert_close("final_state", gc.host(sT.index_select(0, sq).index_select(1, hd)), ref_s[:, heads],
+                    gc.TOL_BF16)
+
+
+def test_prefill_long_1m_sampled():
+    """The pages' 1M-token point: one 1,048,576-token sequence, H=32, d=128,
+    bf16, random initial state, in the library's own segment plan (16,384 chunks
+    per head in segments of 2,049, a 32 GB workspace): heads 0 and 31 computed
+    completely by the oracle."""
+    d = inputs.device_workload_inputs("long_1m")
+    assert d["q"].shape[0] == 1 << 20
+    o, sT = gc.run_prefill(d)
+    heads = [0, 31]
+    hd = torch.tensor(heads, device="cuda")
+    got_o, got_s = gc.host(o.index_select(1, hd)), gc.host(sT.index_select(1, hd))
+    del o, sT
+    torch.cuda.empty_cache()
+    ref_o, ref_s, _ = gc.oracle_prefill(d, heads=heads)
     gc.assert_close("o", got_o, ref_o, gc.TOL_BF16, bf16_rounded=True)
     gc.assert_close("final_state", got_s, ref_s, gc.TOL_BF16)
 
