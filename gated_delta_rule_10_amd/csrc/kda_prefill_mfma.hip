@@ -12,6 +12,8 @@
 //   U' = T Diag(beta) (V - (K . e^G) S)
 //   O  = scale ((Q . e^G) S + P U')
 //   S <- Diag(e^{G_n}) S + (K . e^{G_n-G})^T U'
+// U' enters only those two products, so with B = T Diag(beta), X = V - (K . e^G) S,
+// Y = B^T (K . e^{G_n-G}):  O = scale ((Q . e^G) S + (P B) X),  S <- Diag(e^{G_n}) S + Y^T X.
 //
 // Kernels.
 //  * prep (persistent, all (chunk, head) items in parallel): every quantity that
@@ -24,11 +26,12 @@
 //    channel exceeds e^10 over 16 tokens take an exact fp32 per-element path
 //    for their diagonal block instead. T is inverted in fp32 (forward
 //    substitution on the 16x16 diagonal blocks, fp32 MFMA block recurrence
-//    below them). Results are written to the workspace as fp16 MFMA operand
-//    fragments in exactly the register layout the state passes consume.
+//    below them); Y and P B are fp16 MFMA products of T Diag(beta) with the
+//    decayed keys and with P. Results are written to the workspace as fp16 MFMA
+//    operand fragments in exactly the register layout the state passes consume.
 //  * state passes over segments of consecutive chunks (see below): a map pass,
 //    a prefix over segments and an output pass. The state lives in MFMA
-//    accumulators (fp32); every value-side operand (state, V - K S, U') is
+//    accumulators (fp32); every value-side operand (state, X = V - K S) is
 //    scaled per value column by a power of two before its fp16 conversion, so
 //    the fp16 range never limits the magnitude of v or of the state.
 //
@@ -102,19 +105,21 @@ __device__ __forceinline__ float col_max(float m) {
 }
 
 // Per (chunk, head) record in the workspace; every fragment is 64 lanes x 16 B.
+// With B = T Diag(beta): Y = B^T (K.e^{G_n-G}) and PB = P B, the only two ways the
+// state passes use B (U' = B X enters the state update as (K.e^{G_n-G})^T U' = Y^T X
+// and the outputs as P U' = PB X), so U' itself is never formed.
 template <int K>
 struct Rec {
     static constexpr int NCB = K / 32, NCT = K / 16;
     static constexpr size_t FRAG = 1024;
     static constexpr size_t KEXP = 0;                        // [i 4][cb NCB]  (K.e^G)
     static constexpr size_t QG = KEXP + 4 * NCB * FRAG;      // [i 4][cb NCB]  (Q.e^G)
-    static constexpr size_t KGT = QG + 4 * NCB * FRAG;       // [ct NCT][ks 2] (K.e^{G_n-G})^T
-    static constexpr size_t TM = KGT + 2 * NCT * FRAG;       // 6 lower blocks of T Diag(beta)
-    static constexpr size_t PM = TM + 6 * FRAG;              // 6 lower blocks of P
-    static constexpr size_t GAM = PM + 6 * FRAG;             // e^{G_n} [K] fp32
+    static constexpr size_t YT = QG + 4 * NCB * FRAG;        // [ct NCT][ks 2] Y^T
+    static constexpr size_t PB = YT + 2 * NCT * FRAG;        // 6 lower blocks of P B
+    static constexpr size_t GAM = PB + 6 * FRAG;             // e^{G_n} [K] fp32
     static constexpr size_t BYTES = (GAM + 4 * K + 255) / 256 * 256;
 };
-// (row block i, 32-wide k step ks) -> fragment index for the lower-triangular T and P
+// (row block i, 32-wide k step ks) -> fragment index for the lower-triangular P B
 __device__ __forceinline__ int tri(int i, int ks) { return i < 2 ? i : 2 * i - 2 + ks; }
 // (row block i, column block j <= i) -> B-operand variant of column block j
 __device__ __forceinline__ int vblk(int i, int j) { return (j == 0 ? 0 : j == 1 ? 4 : j == 2 ? 7 : 9) + i - j; }
@@ -180,17 +185,17 @@ struct PrepSmem {
     // accumulator layout (rows 4g + e, column r) and the A-operand reads (row r,
     // columns 4s + g) both spread a wave's 64 lanes over distinct banks
     static constexpr int NCB = K / 32, LD = 68;
-    float tot[4][K];       // decay of each sub-chunk per channel (log, <= 0)
-    float mid[4][K];       // decay from each sub-chunk's start through its 8th token (log, <= 0)
-    float fac[19][K + 4];  // per-channel factors, see prep_kernel
+    _Float16 kgT[K][kC + 8];  // (K.e^{G_n-G}) transposed [channel][token], read last for Y
     float beta[kC];
     float kmax[4];  // max |k_i|, |q_i| over the tokens and channels of each sub-chunk
     union {
-        struct {
+        struct {  // decay factors and the operands of the pairwise products
+            float tot[4][K];          // decay of each sub-chunk per channel (log, <= 0)
+            float mid[4][K];          // decay from each sub-chunk's start through its 8th token (log, <= 0)
+            float fac[19][K + 4];     // per-channel factors, see prep_kernel
             half8 colv[10][NCB][64];  // B operands of the pairwise products
-            _Float16 kgT[K][kC + 8];  // (K.e^{G_n-G}) transposed [channel][token]
         } a;
-        struct {
+        struct {  // then the pairwise matrices and the UT transform
             float A[kC][LD];
             float P[kC][LD];
             float T[kC][LD];
@@ -398,7 +403,7 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
         if (l == 15) sm.kmax[w] = m;
     }
     if (r == 15 || r == 7) {
-        float(*dst)[K] = r == 15 ? sm.tot : sm.mid;
+        float(*dst)[K] = r == 15 ? sm.u.a.tot : sm.u.a.mid;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -425,35 +430,35 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
         int bad = 0;
         if (tid < 2 * K) {
             const int ch = tid & (K - 1);
-            const float d0 = sm.tot[0][ch], d1 = sm.tot[1][ch], d2 = sm.tot[2][ch], d3 = sm.tot[3][ch];
+            const float d0 = sm.u.a.tot[0][ch], d1 = sm.u.a.tot[1][ch], d2 = sm.u.a.tot[2][ch], d3 = sm.u.a.tot[3][ch];
             float mu[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) mu[i] = start_ref ? 0.f : sm.mid[i][ch];
+            for (int i = 0; i < 4; ++i) mu[i] = start_ref ? 0.f : sm.u.a.mid[i][ch];
             if (tid < K) {
                 float emu[4], fd[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     emu[i] = __expf(mu[i]);
                     fd[i] = __expf(fminf(mu[i] - (i == 0 ? d0 : i == 1 ? d1 : i == 2 ? d2 : d3), 80.f));
-                    sm.fac[8 + i][ch] = fd[i];
-                    if (i > 0) sm.fac[11 + i][ch] = emu[i];
+                    sm.u.a.fac[8 + i][ch] = fd[i];
+                    if (i > 0) sm.u.a.fac[11 + i][ch] = emu[i];
                     const float d = i == 0 ? d0 : i == 1 ? d1 : i == 2 ? d2 : d3;
                     bad |= -d > kFastRange || !(sm.kmax[i] <= kFastOperand * emu[i]) ||
                            !(sm.kmax[i] * fd[i] <= kFastOperand);
                 }
-                sm.fac[0][ch] = emu[0];
+                sm.u.a.fac[0][ch] = emu[0];
             } else {
-                sm.fac[1][ch] = __expf(d0 + mu[1]);
-                sm.fac[2][ch] = __expf(d0 + d1 + mu[2]);
-                sm.fac[3][ch] = __expf(d0 + d1 + d2 + mu[3]);
-                sm.fac[4][ch] = __expf(d1 + d2 + d3);
-                sm.fac[5][ch] = __expf(d2 + d3);
-                sm.fac[6][ch] = __expf(d3);
-                sm.fac[7][ch] = 1.f;
-                sm.fac[15][ch] = __expf(d1 + mu[2]);
-                sm.fac[16][ch] = __expf(d2 + mu[3]);
-                sm.fac[17][ch] = __expf(d1 + d2 + mu[3]);
-                sm.fac[18][ch] = __expf(d0 + d1 + d2 + d3);
+                sm.u.a.fac[1][ch] = __expf(d0 + mu[1]);
+                sm.u.a.fac[2][ch] = __expf(d0 + d1 + mu[2]);
+                sm.u.a.fac[3][ch] = __expf(d0 + d1 + d2 + mu[3]);
+                sm.u.a.fac[4][ch] = __expf(d1 + d2 + d3);
+                sm.u.a.fac[5][ch] = __expf(d2 + d3);
+                sm.u.a.fac[6][ch] = __expf(d3);
+                sm.u.a.fac[7][ch] = 1.f;
+                sm.u.a.fac[15][ch] = __expf(d1 + mu[2]);
+                sm.u.a.fac[16][ch] = __expf(d2 + mu[3]);
+                sm.u.a.fac[17][ch] = __expf(d1 + d2 + mu[3]);
+                sm.u.a.fac[18][ch] = __expf(d0 + d1 + d2 + d3);
             }
         }
         return bad;
@@ -464,6 +469,8 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
         (void)factors(true);
         __syncthreads();
     }
+
+    if (tid < K) store_stream(reinterpret_cast<float *>(rec + R::GAM) + tid, sm.u.a.fac[18][tid]);
 
     // ---- elementwise: decayed operands
     half8 kr[NCB], qr[NCB];
@@ -481,14 +488,14 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
     for (int cb = 0; cb < NCB; ++cb) {
         half8 kexp, qg, cv0, cv1, cv2, cv3;
         float tw[8], mw[8], fb[8], fa[8], fi[8], f1[8], f2[8], f3[8];
-        row8(sm.tot[w], cb, tw);
-        row8(sm.mid[w], cb, mw);
-        row8(sm.fac[w], cb, fb);
-        row8(sm.fac[4 + w], cb, fa);
-        row8(sm.fac[8 + w], cb, fi);
-        row8(sm.fac[12 + min(w, 2)], cb, f1);
-        row8(sm.fac[w == 0 ? 15 : 16], cb, f2);
-        row8(sm.fac[17], cb, f3);
+        row8(sm.u.a.tot[w], cb, tw);
+        row8(sm.u.a.mid[w], cb, mw);
+        row8(sm.u.a.fac[w], cb, fb);
+        row8(sm.u.a.fac[4 + w], cb, fa);
+        row8(sm.u.a.fac[8 + w], cb, fi);
+        row8(sm.u.a.fac[12 + min(w, 2)], cb, f1);
+        row8(sm.u.a.fac[w == 0 ? 15 : 16], cb, f2);
+        row8(sm.u.a.fac[17], cb, f3);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int ch = 32 * cb + kidx(g, e);
@@ -502,7 +509,7 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
             kexp[e] = static_cast<_Float16>(krv * fb[e]);
             qg[e] = static_cast<_Float16>(qrv * fb[e]);
             const float kt = kx[cb][e] * tau;
-            sm.u.a.kgT[ch][tr] = static_cast<_Float16>(kt * fa[e]);
+            sm.kgT[ch][tr] = static_cast<_Float16>(kt * fa[e]);
             // column operands of column block w for row blocks i = w..3: k_s e^{G_{m_i} - G_s}
             cv0[e] = static_cast<_Float16>(slow ? 0.f : kt * fi[e]);  // i = w
             cv1[e] = static_cast<_Float16>(kt * f1[e]);                 // i = w + 1
@@ -524,15 +531,6 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
     }
     __syncthreads();
 
-    // ---- (K.e^{G_n-G})^T fragments: [channel tile ct][token step ks]
-    for (int f = w; f < 2 * NCT; f += 4) {
-        const int ct = f >> 1, ks = f & 1;
-        half8 v;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = sm.u.a.kgT[16 * ct + r][32 * ks + kidx(g, e)];
-        store_stream(reinterpret_cast<half8 *>(rec + R::KGT + (f * 64 + l) * 16), v);
-    }
-
     // ---- pairwise products for row block w: A_wj, P_wj, j <= w
     f4 accA[4], accP[4];
 #pragma unroll
@@ -548,7 +546,7 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
             }
         }
     }
-    __syncthreads();  // colv / kgT no longer read; the union now holds A, P, T
+    __syncthreads();  // the factors and colv are no longer read; the union now holds A, P, T
 
     // blocks j <= w of A (strictly lower on the diagonal) and P (lower); the T and P
     // fragments of even row blocks w also span block w + 1, which must read zero
@@ -644,22 +642,91 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
         __syncthreads();
     }
 
-    // ---- T and P fragments of row block w (A operands, contraction over tokens)
+    // ---- Y^T and P B fragments (A operands, contraction over tokens), B = T Diag(beta).
+    // Both are products with B^T on the left, whose rows are tokens: a 16x16 result block
+    // D[4g + e][r] holds for lane (r, g) tokens 4g + e of its block, which is one half of
+    // what a fragment lane holds along the contraction (tokens 4g + e, then 16 + 4g + e),
+    // so the result blocks of tokens 2 ks and 2 ks + 1 make fragment ks.
+    // bt[tb][ks]: rows 16 tb + r of B^T, tokens 32 ks + k(g, e); B^T[t][s] = T[s][t] beta[t]
+    // is zero for s < t (ks < tb / 2 is never used; T's blocks above the diagonal that
+    // the others span were zeroed above).
+    half8 bt[4][2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        if (ks <= (w >> 1)) {
-            half8 tf, pf;
+    for (int tb = 0; tb < 4; ++tb) {
+        const float bb = sm.beta[16 * tb + r];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int col = 32 * ks + kidx(g, e);
-                tf[e] = static_cast<_Float16>(sm.u.b.T[16 * w + r][col] * sm.beta[col]);
-                pf[e] = static_cast<_Float16>(sm.u.b.P[16 * w + r][col]);
+        for (int ks = tb >> 1; ks < 2; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                bt[tb][ks][e] = static_cast<_Float16>(sm.u.b.T[32 * ks + kidx(g, e)][16 * tb + r] * bb);
+    }
+    {  // Y = B^T (K.e^{G_n-G}) for this wave's channel tiles
+        typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+        constexpr int CPW = NCT / 4;
+#pragma unroll
+        for (int q = 0; q < CPW; ++q) {
+            const int ct = w * CPW + q;
+            half8 kf[2];  // B operands: tokens 32 ks + k(g, e) of channel 16 ct + r
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const half4 lo = *reinterpret_cast<const half4 *>(&sm.kgT[16 * ct + r][32 * ks + 4 * g]);
+                const half4 hi = *reinterpret_cast<const half4 *>(&sm.kgT[16 * ct + r][32 * ks + 16 + 4 * g]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    kf[ks][e] = lo[e];
+                    kf[ks][4 + e] = hi[e];
+                }
             }
-            store_stream(reinterpret_cast<half8 *>(rec + R::TM + (tri(w, ks) * 64 + l) * 16), tf);
-            store_stream(reinterpret_cast<half8 *>(rec + R::PM + (tri(w, ks) * 64 + l) * 16), pf);
+            f4 d[4];
+            d[0] = mfma(bt[0][1], kf[1], mfma(bt[0][0], kf[0], zero4()));
+            d[1] = mfma(bt[1][1], kf[1], mfma(bt[1][0], kf[0], zero4()));
+            d[2] = mfma(bt[2][1], kf[1], zero4());
+            d[3] = mfma(bt[3][1], kf[1], zero4());
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                half8 y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    y[e] = static_cast<_Float16>(d[2 * ks][e]);
+                    y[4 + e] = static_cast<_Float16>(d[2 * ks + 1][e]);
+                }
+                store_stream(reinterpret_cast<half8 *>(rec + R::YT + ((ct * 2 + ks) * 64 + l) * 16), y);
+            }
         }
     }
-    if (tid < K) store_stream(reinterpret_cast<float *>(rec + R::GAM) + tid, sm.fac[18][tid]);
+    {  // P B of row block w: (P B)^T blocks (tb, w) = sum_ks bt[tb][ks] P^T, zero for tb > w
+        half8 pf[2] = {};  // B operands: P[16 w + r][32 ks + k(g, e)] (ks = 1 only below row block 2)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            if (ks <= (w >> 1)) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    pf[ks][e] = static_cast<_Float16>(sm.u.b.P[16 * w + r][32 * ks + kidx(g, e)]);
+            }
+        }
+        f4 d[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            d[tb] = zero4();
+            if (tb <= w) {
+#pragma unroll
+                for (int ks = tb >> 1; ks < 2; ++ks)
+                    if (ks <= (w >> 1)) d[tb] = mfma(bt[tb][ks], pf[ks], d[tb]);
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            if (ks <= (w >> 1)) {
+                half8 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = static_cast<_Float16>(d[2 * ks][e]);
+                    v[4 + e] = static_cast<_Float16>(d[2 * ks + 1][e]);
+                }
+                store_stream(reinterpret_cast<half8 *>(rec + R::PB + (tri(w, ks) * 64 + l) * 16), v);
+            }
+        }
+    }
     raw.activate(a.gscale);  // the next item's gates
     kqmax = raw.absmax();     // and the magnitude of its k, q
     __syncthreads();  // the next item rewrites the LDS this one read last
@@ -669,7 +736,7 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
 // ---------------------------------------------------------------------------
 // State passes. The chunks of a sequence are cut into segments of L consecutive
 // chunks. Every chunk maps its incoming state affinely,
-//   S <- (Diag(e^{G_n}) - (K.e^{G_n-G})^T T Diag(beta) (K.e^G)) S + (K.e^{G_n-G})^T T Diag(beta) V,
+//   S <- (Diag(e^{G_n}) - Y^T (K.e^G)) S + Y^T V,
 // so a segment does too: S_out = M S_in + N, with M (d_k x d_k) the segment run
 // from the identity with V = 0 and N (d_k x d_v) the segment run from zero.
 //  * seg_kernel, every segment but the last of each sequence, in parallel:
@@ -755,10 +822,9 @@ __device__ __forceinline__ void dma4(const void *base, uint32_t voff, const char
 #pragma clang diagnostic pop
 
 // Copy chunk data into LDS buffer `dst`, spread over the NW waves: the record
-// fragments the pass reads (all of them with outputs, else K.e^G, its transpose
-// with e^{G_n-G}, and T Diag(beta)), e^{G_n}, and (HASV) the 64 x V tile of V.
-// Tokens past the sequence end read the last token (finite; their columns of
-// T Diag(beta) are zero).
+// fragments the pass reads (all of them with outputs, else K.e^G and Y^T), e^{G_n},
+// and (HASV) the 64 x V tile of V. Tokens past the sequence end read the last token
+// (finite; their columns of Y^T and P B are zero).
 // PART (with FULL): 0 = the whole record, 1 = only K.e^G and Q.e^G (copied early),
 // 2 = everything but K.e^G and Q.e^G.
 template <int K, int V, bool FULL, bool HASV, int NW, int PART = 0>
@@ -766,8 +832,8 @@ __device__ __forceinline__ void copy_chunk(char *dst, const char *rec, const bf1
                                            int H, int h, int w, int l) {
     using R = Rec<K>;
     constexpr int NKX = 4 * (K / 32);
-    constexpr int KG0 = static_cast<int>(R::KGT / 1024);
-    constexpr int NF = FULL ? static_cast<int>(R::GAM / 1024) : NKX + 2 * (K / 16) + 6;
+    constexpr int KG0 = static_cast<int>(R::YT / 1024);
+    constexpr int NF = FULL ? static_cast<int>(R::GAM / 1024) : NKX + 2 * (K / 16);
     static_assert(PART == 0 || FULL, "parts of the full record only");
     constexpr int F0 = PART == 2 ? KG0 : 0, F1 = PART == 1 ? KG0 : NF;
     const uint32_t lo = static_cast<uint32_t>(l) * 16u;
@@ -825,9 +891,8 @@ __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F);
 // One chunk for one wave holding NB 16-column blocks of the state, S[j][ct] =
 // rows 16 ct + 4g + e of column col0 + 16 j + r. part_a: column scales of the
 // state, (K.e^G) S and (OUT) (Q.e^G) S, and X = V - (K.e^G) S as scaled fp16
-// operands (V = 0 without HASV). part_b: U' = (T Diag(beta)) X (beta is folded
-// into the record's T fragments), the state update and (OUT) the outputs
-// O = (Q.e^G) S + P U' of tokens 16i + 4g + e in out[j][i].
+// operands (V = 0 without HASV). part_b: the state update S <- Diag(e^{G_n}) S + Y^T X
+// and (OUT) the outputs O = (Q.e^G) S + (P B) X of tokens 16i + 4g + e in out[j][i].
 template <int K, int V, int NB, bool OUT, bool HASV>
 struct ChunkStep {
     static constexpr int NCB = K / 32, NCT = K / 16;
@@ -907,62 +972,33 @@ struct ChunkStep {
 
     __device__ __forceinline__ void part_b(const char *buf, lds_cchar *fb, f4 (&S)[NB][NCT], f4 (&out)[NB][4],
                                            float scale, int g) {
-        half8 tm[6];
-#pragma unroll
-        for (int f = 0; f < 6; ++f) tm[f] = lds_frag(fb, R::TM + f * 1024);
-        half8 uf[NB][2];
-        float sigu[NB];
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            // U' = T X, held as U' / sigx
-            f4 U[4];
-            U[0] = mfma(tm[0], xf[j][0], zero4());
-            U[1] = mfma(tm[1], xf[j][0], zero4());
-            U[2] = mfma(tm[3], xf[j][1], mfma(tm[2], xf[j][0], zero4()));
-            U[3] = mfma(tm[5], xf[j][1], mfma(tm[4], xf[j][0], zero4()));
-            float mu = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) mu = fmaxf(mu, fabsf(U[i][e]));
-            float invu;
-            sigu[j] = col_scale(col_max(mu) * sigx[j], invu);
-            const float ru = sigx[j] * invu;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    uf[j][ks][e] = static_cast<_Float16>(U[2 * ks][e] * ru);
-                    uf[j][ks][4 + e] = static_cast<_Float16>(U[2 * ks + 1][e] * ru);
-                }
-        }
-        // S <- Diag(e^{G_n}) S + (K.e^{G_n-G})^T U'
+        // S <- Diag(e^{G_n}) S + Y^T X  (X held as X / sigx)
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             const f4 gm = *reinterpret_cast<const f4 *>(buf + R::GAM + (16 * ct + 4 * g) * 4);
-            const half8 k0 = lds_frag(fb, R::KGT + (ct * 2 + 0) * 1024);
-            const half8 k1 = lds_frag(fb, R::KGT + (ct * 2 + 1) * 1024);
+            const half8 y0 = lds_frag(fb, R::YT + (ct * 2 + 0) * 1024);
+            const half8 y1 = lds_frag(fb, R::YT + (ct * 2 + 1) * 1024);
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
-                const f4 acc = mfma(k1, uf[j][1], mfma(k0, uf[j][0], zero4()));
+                const f4 acc = mfma(y1, xf[j][1], mfma(y0, xf[j][0], zero4()));
 #pragma unroll
-                for (int e = 0; e < 4; ++e) S[j][ct][e] = fmaf(sigu[j], acc[e], S[j][ct][e] * gm[e]);
+                for (int e = 0; e < 4; ++e) S[j][ct][e] = fmaf(sigx[j], acc[e], S[j][ct][e] * gm[e]);
             }
         }
         if (OUT) {
-            // O = (Q.e^G) S + P U'
+            // O = (Q.e^G) S + (P B) X
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const half8 p0 = lds_frag(fb, R::PM + tri(i, 0) * 1024);
+                const half8 p0 = lds_frag(fb, R::PB + tri(i, 0) * 1024);
                 half8 p1 = p0;
-                if (i >= 2) p1 = lds_frag(fb, R::PM + tri(i, 1) * 1024);
+                if (i >= 2) p1 = lds_frag(fb, R::PB + tri(i, 1) * 1024);
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
-                    f4 pu = mfma(p0, uf[j][0], zero4());
-                    if (i >= 2) pu = mfma(p1, uf[j][1], pu);
-                    const float os = sigs[j] * scale, ou = sigu[j] * scale;
+                    f4 px = mfma(p0, xf[j][0], zero4());
+                    if (i >= 2) px = mfma(p1, xf[j][1], px);
+                    const float os = sigs[j] * scale, ox = sigx[j] * scale;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) out[j][i][e] = fmaf(oa[j][i][e], os, pu[e] * ou);
+                    for (int e = 0; e < 4; ++e) out[j][i][e] = fmaf(oa[j][i][e], os, px[e] * ox);
                 }
             }
         }
@@ -1395,7 +1431,7 @@ __global__ __launch_bounds__(64 * V / 16) void out_kernel(PrefillArgs a, const i
                                                           int L, const char *recs, SegBufs sb) {
     constexpr int NB = 1, NW = V / 16;
     // the fp32 epilogue tile goes into the K.e^G / Q.e^G region of a chunk buffer when it fits
-    constexpr bool FTD = EPI && static_cast<size_t>(kC) * V * 4 > Rec<K>::KGT;
+    constexpr bool FTD = EPI && static_cast<size_t>(kC) * V * 4 > Rec<K>::YT;
     __shared__ __attribute__((aligned(16))) char lb0[ScanBuf<K, V>::BYTES];
     __shared__ __attribute__((aligned(16))) char lb1[ScanBuf<K, V>::BYTES];
     __shared__ __attribute__((aligned(16))) char ftd[FTD ? kC * V * 4 : 16];
