@@ -270,3 +270,81 @@ def test_prefill_replayed_from_a_hip_graph_matches_eager(monkeypatch):
         for t, r in zip(o + fin, ref):
             assert torch.equal(t, r), f"replay {rep}: differs from eager"
         _ = (s0 * 2).sum().item()   # eager work between replays
+
+
+def _row_err(got, ref):
+    """max over output rows (one token or sequence, one head) of max |got - ref| / RMS(ref) of the row"""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    rms = np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True))
+    return float(np.max(np.abs(got - ref) / np.maximum(rms, 1e-30)))
+
+
+def _epilogue_ref(raw, x, norm, z_act):
+    ref = np.asarray(raw, np.float64)
+    if norm:
+        ref = oo.rms_norm(ref, 1e-5, x["norm_weight"])
+    if z_act is not None:
+        ref = oo.output_gate(ref, x["out_gate"], z_act)
+    return ref
+
+
+def _epilogue_kw(x, bf, norm, z_act):
+    kw = {}
+    if norm:
+        kw.update(norm=True, norm_eps=1e-5, norm_weight=_t(x["norm_weight"], False))
+    if z_act is not None:
+        kw.update(out_gate=_t(x["out_gate"], bf), out_gate_act=z_act)
+    return kw
+
+
+EPI_CASES = [(True, None), (False, "sigmoid"), (True, "none"), (True, "sigmoid")]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("norm,z_act", EPI_CASES)
+def test_epilogue_arithmetic_prefill(dt, norm, z_act, monkeypatch):
+    """The fused RMS-norm / output-gate epilogue of the prefill against the oracle's
+    rms_norm and output_gate applied in fp64 to the same kernels' fp32 output
+    without the epilogue, from the same inputs (identical up to the epilogue): only
+    the epilogue's own fp32 arithmetic separates the two, held to 1e-5 of each
+    row's RMS. The parity tests above hold the whole path to the oracle."""
+    monkeypatch.setenv("KDA_SEG_CHUNKS", "2")
+    bf = dt == "bf16"
+    lens = [190, 64, 1, 333]
+    T, Hk, H, K, V = int(sum(lens)), 2, 4, 128, 128
+    x = inputs.option_inputs(31, T, Hk, H, K, V, dt)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).cuda()
+    g = (-0.1 * oo.softplus(x["gate_x"])).astype(np.float32)
+    b = oo.sigmoid(x["beta_y"]).astype(np.float32)
+    s0 = (0.02 * np.random.default_rng(32).standard_normal((len(lens), H, K, V))).astype(np.float32)
+    q, k, v = _t(x["q"], bf), _t(x["k"], bf), _t(x["v"], bf)
+    common = dict(log_alpha=_t(g, False), beta=_t(b, False), initial_state=_t(s0, False), out_dtype=torch.float32)
+    raw, _ = kda.kda_chunk_fwd_ex(q, k, v, cu, **common)
+    epi, _ = kda.kda_chunk_fwd_ex(q, k, v, cu, **common, **_epilogue_kw(x, bf, norm, z_act))
+    torch.cuda.synchronize()
+    err = _row_err(gc.host(epi), _epilogue_ref(gc.host(raw), x, norm, z_act))
+    print(f"prefill epilogue {dt} norm={norm} z={z_act}: max err / row RMS {err:.2e}")
+    assert err <= 1e-5
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("norm,z_act", EPI_CASES)
+def test_epilogue_arithmetic_decode(dt, norm, z_act):
+    """As above for one decode step (each call on its own copy of the state cache).
+    With the norm the decode kernel keeps whole rows in one workgroup, so its column
+    sums over d_k are grouped differently from the call without it: a difference of
+    the order of the fp32 rounding of those sums, far below the 1e-5 bar."""
+    bf = dt == "bf16"
+    B, Hk, H, K, V = 16, 2, 4, 128, 128
+    x = inputs.option_inputs(33, B, Hk, H, K, V, dt)
+    g = (-0.1 * oo.softplus(x["gate_x"])).astype(np.float32)
+    b = oo.sigmoid(x["beta_y"]).astype(np.float32)
+    state = torch.from_numpy((0.02 * np.random.default_rng(34).standard_normal((B, H, K, V))).astype(np.float32)).cuda()
+    q, k, v = _t(x["q"], bf), _t(x["k"], bf), _t(x["v"], bf)
+    common = dict(log_alpha=_t(g, False), beta=_t(b, False), out_dtype=torch.float32)
+    raw = kda.kda_decode_step_ex(q, k, v, state.clone(), **common)
+    epi = kda.kda_decode_step_ex(q, k, v, state.clone(), **common, **_epilogue_kw(x, bf, norm, z_act))
+    torch.cuda.synchronize()
+    err = _row_err(gc.host(epi), _epilogue_ref(gc.host(raw), x, norm, z_act))
+    print(f"decode epilogue {dt} norm={norm} z={z_act}: max err / row RMS {err:.2e}")
+    assert err <= 1e-5
