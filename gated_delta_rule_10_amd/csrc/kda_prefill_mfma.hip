@@ -1046,9 +1046,12 @@ __device__ __forceinline__ void run_segment(char *lb0, char *lb1, char *ftd, f4 
     using VT = VTile<V>;
     // With bf16 output tiles (no epilogue, whose fp32 tile reuses that region), the
     // K.e^G and Q.e^G fragments of chunk c + 2 are copied into chunk c's buffer as soon
-    // as chunk c has read them, and the rest at chunk c + 1: each copy wave then has
-    // exactly EW early copies in flight while it waits for chunk c + 1 (the vector-memory
-    // counter retires this wave's loads and stores in the order they were issued).
+    // as chunk c has read them, and the rest at chunk c + 1. A copy wave then waits for
+    // chunk c + 1 with vmcnt(EW): its last vector-memory operations are the EW early
+    // copies, and the counter also counts its output stores, so at most EW loads are then
+    // outstanding whatever the order in which stores retire. Loads retire in the order
+    // they were issued (the rule every partial vmcnt wait rests on), so those are the
+    // early copies, and every copy of chunk c + 1 has landed.
     constexpr bool LA = OUT && TILE && !EPI && COPYV;
     constexpr int EW = LA ? 8 * (K / 32) / CW : 0;
     static_assert(!LA || (8 * (K / 32)) % CW == 0, "early copies spread evenly over the copy waves");

@@ -187,7 +187,7 @@ def test_prefill_varlen_512k_sampled():
 def test_prefill_long_1m_sampled():
     """The pages' 1M-token point: one 1,048,576-token sequence, H=32, d=128,
     bf16, random initial state, in the library's own segment plan (16,384 chunks
-    per head in segments of 2,049, a 32 GB workspace): heads 0 and 31 computed
+    per head in segments of 2,049, a 29 GB workspace): heads 0 and 31 computed
     completely by the oracle."""
     d = inputs.device_workload_inputs("long_1m")
     assert d["q"].shape[0] == 1 << 20

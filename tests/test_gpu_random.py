@@ -68,13 +68,12 @@ def _large_config(i):
 @pytest.mark.parametrize("i", range(8))
 def test_random_large_configuration(i, monkeypatch):
     """Up to 8 sequences of up to 20K tokens, H up to 32, bf16, with the library's
-    own segment length and choice of streams."""
-    import torch
+    own segment length; bf16 outputs, and fp32 outputs held to the bar directly."""
     monkeypatch.delenv("KDA_SEG_CHUNKS", raising=False)
     c = _large_config(i)
     print(f"  large case {i}: T={sum(c['lens'])} {c}", flush=True)
     _prefill_case(8000 + i, c["lens"], c["Hk"], c["H"], c["K"], c["V"], "bf16", gates=c["gates"], norm=c["norm"],
-                  z_act=c["z_act"], slots=c["slots"], decay=c["decay"], out_dtypes=[torch.bfloat16])
+                  z_act=c["z_act"], slots=c["slots"], decay=c["decay"])
 
 
 def _decode_config(i):
