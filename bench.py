@@ -162,7 +162,7 @@ def err_over_rms(got, ref, bf16_out):
         ax = np.maximum(np.abs(ref), np.abs(got))
         e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
         d = np.maximum(d - np.where(ax > 0, np.exp2(e - 8.0), 0.0), 0.0)
-    return float(d.max() / max(float(np.sqrt(np.mean(ref * ref))), 1e-30))
+    return float(d.max() / max(float(np.sqrt(np.mean(ref * ref))), 1e-300))
 
 
 def cpu_baseline_decode(d, target_s=5.0):

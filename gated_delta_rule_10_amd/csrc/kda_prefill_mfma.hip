@@ -341,13 +341,18 @@ struct PrepRaw {
                 qx[cb][2 * e + 1] = __uint_as_float(qw[e] & 0xFFFF0000u);
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                sc[cb][e] = valid ? gg[e] : 0.f;
-                if (!valid) {
-                    kx[cb][e] = 0.f;
-                    qx[cb][e] = 0.f;
+            for (int e = 0; e < 8; ++e) sc[cb][e] = gg[e];
+        }
+        // tokens past the sequence end (only in a sequence's last chunk: a wave-uniform branch)
+        if (__builtin_amdgcn_ballot_w64(!valid) != 0) {
+#pragma unroll
+            for (int cb = 0; cb < K / 32; ++cb)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    sc[cb][e] = valid ? sc[cb][e] : 0.f;
+                    kx[cb][e] = valid ? kx[cb][e] : 0.f;
+                    qx[cb][e] = valid ? qx[cb][e] : 0.f;
                 }
-            }
         }
 #pragma unroll
         for (int cb = 0; cb < K / 32; ++cb)
@@ -434,6 +439,10 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
             float mu[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) mu[i] = start_ref ? 0.f : sm.u.a.mid[i][ch];
+            if (start_ref && tid < K) {  // the elementwise phase reads the reference from mid
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm.u.a.mid[i][ch] = 0.f;
+            }
             if (tid < K) {
                 float emu[4], fd[4];
 #pragma unroll
@@ -500,8 +509,8 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
         for (int e = 0; e < 8; ++e) {
             const int ch = 32 * cb + kidx(g, e);
             // e^{G_r - G_m} (m: the reference of this row's products; at most e^{8-token decay}
-            // on the fast path, <= 1 from the sub-chunk start on the slow path)
-            const float rho = __expf(s[cb][e] - (slow ? 0.f : mw[e]));
+            // on the fast path, <= 1 from the sub-chunk start on the slow path, where mid is 0)
+            const float rho = __expf(s[cb][e] - mw[e]);
             const float tau = __expf(tw[e] - s[cb][e]);  // e^{G_{b'} - G_r} <= 1, b' = sub-chunk end
             const float krv = kx[cb][e] * rho, qrv = qx[cb][e] * rho;
             kr[cb][e] = static_cast<_Float16>(krv);
@@ -511,7 +520,8 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
             const float kt = kx[cb][e] * tau;
             sm.kgT[ch][tr] = static_cast<_Float16>(kt * fa[e]);
             // column operands of column block w for row blocks i = w..3: k_s e^{G_{m_i} - G_s}
-            cv0[e] = static_cast<_Float16>(slow ? 0.f : kt * fi[e]);  // i = w
+            // (i = w on the slow path: unbounded, but its products are replaced by the exact ones)
+            cv0[e] = static_cast<_Float16>(kt * fi[e]);                 // i = w
             cv1[e] = static_cast<_Float16>(kt * f1[e]);                 // i = w + 1
             cv2[e] = static_cast<_Float16>(kt * f2[e]);                 // i = w + 2
             cv3[e] = static_cast<_Float16>(kt * f3[e]);                 // i = 3 (w = 0)
@@ -889,36 +899,74 @@ __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }   
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }    // lgkmcnt(0)
 
 // One chunk for one wave holding NB 16-column blocks of the state, S[j][ct] =
-// rows 16 ct + 4g + e of column col0 + 16 j + r. part_a: column scales of the
-// state, (K.e^G) S and (OUT) (Q.e^G) S, and X = V - (K.e^G) S as scaled fp16
-// operands (V = 0 without HASV). part_b: the state update S <- Diag(e^{G_n}) S + Y^T X
-// and (OUT) the outputs O = (Q.e^G) S + (P B) X of tokens 16i + 4g + e in out[j][i].
+// rows 16 ct + 4g + e of column col0 + 16 j + r, held as S / sc[j] with a power of
+// two sc[j] per column (ChunkScale) that changes only when the held values leave the
+// range of their fp16 conversion. part_a: (K.e^G) S and (OUT) (Q.e^G) S, and
+// X = V - (K.e^G) S as a scaled fp16 operand (V = 0 without HASV). part_b: the state
+// update S <- Diag(e^{G_n}) S + Y^T X and (OUT) the outputs O = (Q.e^G) S + (P B) X of
+// tokens 16i + 4g + e in out[j][i].
+template <int NB>
+struct ChunkScale {
+    float sc[NB], isc[NB];  // sc and 1 / sc, both powers of two
+    __device__ __forceinline__ ChunkScale() {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) sc[j] = isc[j] = 1.f;
+    }
+};
 template <int K, int V, int NB, bool OUT, bool HASV>
 struct ChunkStep {
     static constexpr int NCB = K / 32, NCT = K / 16;
     using R = Rec<K>;
-    float sigs[NB], sigx[NB];
+    float sigs[NB], sigx[NB], ix[NB];  // ix = 1 / sigx
     half8 xf[NB][2];
     f4 oa[NB][4];
 
-    __device__ __forceinline__ void part_a(const char *buf, lds_cchar *fb, const f4 (&S)[NB][NCT], int col0, int l, int r,
-                                           int g) {
+    // The held values are the fp16 operand itself while every column's largest magnitude
+    // lies in [2^-13, 2^15): below 2^-14 an element is subnormal in fp16, and its absolute
+    // error (2^-25 at most) stays under half an fp16 ulp of that largest magnitude. When a
+    // column of the wave leaves the range, its columns are brought to [2^14, 2^15) (a
+    // wave-uniform branch, rare once a state has formed). The scale is that of col_scale,
+    // within [2^-114, 2^96]: a column whose true magnitude falls below 2^-127 (a map
+    // decayed away) keeps sc = 2^-114 and fits as it is, and zero columns fit.
+    __device__ __forceinline__ void part_a(const char *buf, lds_cchar *fb, f4 (&S)[NB][NCT], ChunkScale<NB> &cs,
+                                           int col0, int l, int r, int g) {
         half8 sf[NB][NCB];
+        float m[NB];
+        bool fit = true;
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-            float m = 0.f;
+            float mj = 0.f;
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(S[j][ct][e]));
-            float inv;
-            sigs[j] = col_scale(col_max(m), inv);
+                for (int e = 0; e < 4; ++e) mj = fmaxf(mj, fabsf(S[j][ct][e]));
+            m[j] = col_max(mj);
+            fit = fit && m[j] < 0x1p15f && (m[j] >= 0x1p-13f || m[j] == 0.f || cs.sc[j] == 0x1p-114f);
+        }
+        if (__builtin_amdgcn_ballot_w64(!fit) != 0) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                if (m[j] > 0.f) {
+                    float inv;
+                    const float s = col_scale(m[j] * cs.sc[j], inv);
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) S[j][ct][e] = (S[j][ct][e] * cs.sc[j]) * inv;
+                    cs.sc[j] = s;
+                    cs.isc[j] = inv;
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            sigs[j] = cs.sc[j];
 #pragma unroll
             for (int kb = 0; kb < NCB; ++kb)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    sf[j][kb][e] = static_cast<_Float16>(S[j][2 * kb][e] * inv);
-                    sf[j][kb][4 + e] = static_cast<_Float16>(S[j][2 * kb + 1][e] * inv);
+                    sf[j][kb][e] = static_cast<_Float16>(S[j][2 * kb][e]);
+                    sf[j][kb][4 + e] = static_cast<_Float16>(S[j][2 * kb + 1][e]);
                 }
         }
         f4 xa[NB][4];
@@ -960,6 +1008,7 @@ struct ChunkStep {
             }
             float invx;
             sigx[j] = col_scale(col_max(mx), invx);
+            ix[j] = invx;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -970,9 +1019,32 @@ struct ChunkStep {
         }
     }
 
-    __device__ __forceinline__ void part_b(const char *buf, lds_cchar *fb, f4 (&S)[NB][NCT], f4 (&out)[NB][4],
-                                           float scale, int g) {
-        // S <- Diag(e^{G_n}) S + Y^T X  (X held as X / sigx)
+    __device__ __forceinline__ void part_b(const char *buf, lds_cchar *fb, f4 (&S)[NB][NCT], ChunkScale<NB> &cs,
+                                           f4 (&out)[NB][4], float scale, int g) {
+        // S <- Diag(e^{G_n}) S + Y^T X  (X held as X / sigx, S as S / sc). An update more
+        // than 2^100 times the held state's scale restarts that column's scale at sigx (the
+        // state is then negligible beside it), so that sigx / sc stays finite.
+        float fx[NB];
+        bool big = false;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            fx[j] = sigx[j] * cs.isc[j];
+            big = big || !(fx[j] <= 0x1p100f);
+        }
+        if (__builtin_amdgcn_ballot_w64(big) != 0) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                if (!(fx[j] <= 0x1p100f)) {
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) S[j][ct][e] = (S[j][ct][e] * cs.sc[j]) * ix[j];
+                    cs.sc[j] = sigx[j];
+                    cs.isc[j] = ix[j];
+                    fx[j] = 1.f;
+                }
+            }
+        }
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             const f4 gm = *reinterpret_cast<const f4 *>(buf + R::GAM + (16 * ct + 4 * g) * 4);
@@ -982,7 +1054,7 @@ struct ChunkStep {
             for (int j = 0; j < NB; ++j) {
                 const f4 acc = mfma(y1, xf[j][1], mfma(y0, xf[j][0], zero4()));
 #pragma unroll
-                for (int e = 0; e < 4; ++e) S[j][ct][e] = fmaf(sigx[j], acc[e], S[j][ct][e] * gm[e]);
+                for (int e = 0; e < 4; ++e) S[j][ct][e] = fmaf(fx[j], acc[e], S[j][ct][e] * gm[e]);
             }
         }
         if (OUT) {
@@ -1058,6 +1130,7 @@ __device__ __forceinline__ void run_segment(char *lb0, char *lb1, char *ftd, f4 
     static_assert(EW <= 15, "early copies within the low vmcnt field");
     if (cb >= ce) return;
     f4 out[NB][4];
+    ChunkScale<NB> cs;  // the state is held as S / cs.sc across the chunks (ChunkStep)
     if (w < CW) copy_chunk<K, V, OUT, COPYV, CW>(lb0, hrec + static_cast<size_t>(cb) * RB, vg, tbeg, tend, H, h, w, l);
 
     // epilogue: this thread's row and 16 columns of the fp32 tile, its weights, and
@@ -1176,14 +1249,14 @@ __device__ __forceinline__ void run_segment(char *lb0, char *lb1, char *ftd, f4 
             }
         }
         ChunkStep<K, V, NB, OUT, HASV> st;
-        if (active) st.part_a(cur, fbc, S, col0, l, r, g);
+        if (active) st.part_a(cur, fbc, S, cs, col0, l, r, g);
         if (TILE) wg_barrier();  // every wave has read K.e^G, Q.e^G and V of chunk c: the tile may go there
         if constexpr (LA) {
             if (c + 2 < ce && w < CW)
                 copy_chunk<K, V, OUT, COPYV, CW, 1>(cur, hrec + static_cast<size_t>(c + 2) * RB, vg, tc + 2 * kC, tend, H,
                                                     h, w, l);
         }
-        if (active) st.part_b(cur, fbc, S, out, scale, g);
+        if (active) st.part_b(cur, fbc, S, cs, out, scale, g);
         if (OUT && active) {
 #pragma unroll
             for (int j = 0; j < NB; ++j)
@@ -1210,6 +1283,12 @@ __device__ __forceinline__ void run_segment(char *lb0, char *lb1, char *ftd, f4 
         if (c + 1 >= ce) break;
         body(lb1, fb1, lb0, c + 1);
     }
+#pragma unroll
+    for (int j = 0; j < NB; ++j)  // the state itself for the caller
+#pragma unroll
+        for (int ct = 0; ct < K / 16; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[j][ct][e] *= cs.sc[j];
     if (TILE) {
         wait_all();
         wg_barrier();

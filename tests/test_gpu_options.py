@@ -276,7 +276,7 @@ def _row_err(got, ref):
     """max over output rows (one token or sequence, one head) of max |got - ref| / RMS(ref) of the row"""
     got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
     rms = np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True))
-    return float(np.max(np.abs(got - ref) / np.maximum(rms, 1e-30)))
+    return float(np.max(np.abs(got - ref) / np.maximum(rms, 1e-300)))
 
 
 def _epilogue_ref(raw, x, norm, z_act):

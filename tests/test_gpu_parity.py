@@ -145,6 +145,35 @@ def test_prefill_segmented_head_dims(dk, dv, monkeypatch):
     _prefill_case(inputs.prefill_inputs(12, [520, 70, 300], 2, dk, dv, "bf16", 0.1, "random"))
 
 
+@pytest.mark.parametrize("decay,seg", [(3.0, "24"), (0.1, "24"), (0.1, None)])
+def test_prefill_long_segments_with_decay(decay, seg, monkeypatch):
+    """Segments of many chunks, so that the map pass's M (the identity carried through
+    a segment) decays far below the fp32 range: within two chunks with strong gates
+    (decay 3.0, alpha down to ~e^-6 per token), gradually over the 24-chunk segments
+    with the default gates, and in the library's own plan."""
+    if seg is None:
+        monkeypatch.delenv("KDA_SEG_CHUNKS", raising=False)
+    else:
+        monkeypatch.setenv("KDA_SEG_CHUNKS", seg)
+    _prefill_case(inputs.prefill_inputs(13, [3000, 1700, 45], 2, 128, 128, "bf16", decay, "random"))
+
+
+@pytest.mark.parametrize("c", [2.0 ** -110, 2.0 ** -40, 2.0 ** 40, 2.0 ** 100])
+def test_prefill_value_magnitudes(c, monkeypatch):
+    """v and the initial state scaled by a power of two c (the bf16 values stay exact):
+    in the oracle o and the final state scale by c exactly, and the kernels, whose
+    value-side fp16 operands are scaled per column, meet the same relative bar."""
+    monkeypatch.setenv("KDA_SEG_CHUNKS", "4")
+    inp = inputs.prefill_inputs(14, [700, 333], 2, 128, 128, "bf16", 0.1, "random")
+    d = gc.to_device(inp)
+    ref_o, ref_s, _ = gc.oracle_prefill(d)
+    d = dict(d, v=d["v"] * c, initial_state=d["initial_state"] * c)
+    for od in (torch.bfloat16, torch.float32):
+        o, sT = gc.run_prefill(d, out_dtype=od)
+        gc.assert_close(f"o[{od}] x {c:.1e}", gc.host(o), ref_o * c, gc.TOL_BF16, bf16_rounded=od == torch.bfloat16)
+        gc.assert_close(f"final_state x {c:.1e}", gc.host(sT), ref_s * c, gc.TOL_BF16)
+
+
 def test_prefill_long_128k_sampled():
     """One 131072-token sequence, H=32, d=128, bf16, random initial state:
     heads 0 and 31 computed completely by the oracle, for bf16 outputs and for
