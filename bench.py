@@ -44,13 +44,13 @@ def prefill_flops_per_token_head(K, V, c=C):
             + c ** 3 / 3 + 6 * c * K * V) / c
 
 
-def fused_prefill_bytes(T, H, K, V, N, in_bytes=2, out_bytes=2):
-    """Algorithmic bytes of the extended call with gate pre-activations and the
-    output epilogue: q, k, v, gate_x ([T,H,K]), beta_y ([T,H]) and the output gate
-    z ([T,H,V]) read once in the input type, o written once, the d_v norm
-    weight, and the initial and final states."""
-    per_tok_head = (3 * K + V + 1 + V) * in_bytes + V * out_bytes
-    return T * H * per_tok_head + 4 * V + N * H * K * V * 4 * 2
+def fused_prefill_bytes(T, H, K, V, N, in_bytes=2, out_bytes=2, epilogue=True):
+    """Algorithmic bytes of the extended call with gate pre-activations: q, k, v,
+    gate_x ([T,H,K]), beta_y ([T,H]) and, with the output epilogue, the output gate
+    z ([T,H,V]) read once in the input type, o written once, the d_v norm weight,
+    and the initial and final states."""
+    per_tok_head = (3 * K + V + 1 + (V if epilogue else 0)) * in_bytes + V * out_bytes
+    return T * H * per_tok_head + (4 * V if epilogue else 0) + N * H * K * V * 4 * 2
 
 
 def time_calls(fn, steps, warmup, stream):
@@ -344,15 +344,24 @@ def main():
                                  out_gate_act="sigmoid", initial_state=d["initial_state"], final_state=sT,
                                  o=o, stream=stream)
 
-        fms = time_calls(fused, args.steps, args.warmup, stream)
-        fb = fused_prefill_bytes(T, H, K, V, N)
-        fgbs = fb / (fms / 1e3) / 1e9
-        result["variants"] = {"fused_gates_norm_gate": {
-            "entry": "kda_chunk_fwd_ex (gate_x, beta_y bf16; norm + weight; sigmoid output gate)",
-            "workload": name, "ms_per_step": round(fms, 4), "value": round(T / (fms / 1e3) / 1e6, 3),
-            "unit": "Mtokens/s",
-            "roofline": {"bound": "hbm", "achieved": round(fgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(fgbs / PEAK_HBM_GBS, 4), "algorithmic_bytes_per_launch": fb}}}
+        def gates_only():
+            kda.kda_chunk_fwd_ex(d["q"], d["k"], d["v"], d["cu_seqlens"], gate_x=gx, beta_y=by,
+                                 gate_scale=0.05, initial_state=d["initial_state"], final_state=sT, o=o,
+                                 stream=stream)
+
+        result["variants"] = {}
+        for vname, fn, entry, epi in (
+                ("fused_gates_norm_gate", fused,
+                 "kda_chunk_fwd_ex (gate_x, beta_y bf16; norm + weight; sigmoid output gate)", True),
+                ("fused_gates", gates_only, "kda_chunk_fwd_ex (gate_x, beta_y bf16; no epilogue)", False)):
+            fms = time_calls(fn, args.steps, args.warmup, stream)
+            fb = fused_prefill_bytes(T, H, K, V, N, epilogue=epi)
+            fgbs = fb / (fms / 1e3) / 1e9
+            result["variants"][vname] = {
+                "entry": entry, "workload": name, "ms_per_step": round(fms, 4),
+                "value": round(T / (fms / 1e3) / 1e6, 3), "unit": "Mtokens/s",
+                "roofline": {"bound": "hbm", "achieved": round(fgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": round(fgbs / PEAK_HBM_GBS, 4), "algorithmic_bytes_per_launch": fb}}
         del gx, by, z
 
     cpu_d = None
