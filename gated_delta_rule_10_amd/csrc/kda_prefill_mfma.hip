@@ -757,8 +757,8 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
 //  * out_kernel, every segment in parallel from its incoming state, with outputs;
 //    the last segment of a sequence writes the final state.
 // A workgroup covers all columns of one (segment, head) state (and of M); each
-// wave holds 16 columns x d_k rows in MFMA accumulators (four waves per SIMD in
-// the map pass, two in the output pass). A chunk's record is copied global -> LDS once per workgroup with
+// wave holds d_k rows of 32 columns (map pass) or 16 (output pass) in MFMA
+// accumulators, two waves per SIMD. A chunk's record is copied global -> LDS once per workgroup with
 // direct-to-LDS loads, one chunk ahead, into a two-buffer ring (the output pass
 // starts K.e^G and Q.e^G of the chunk after next too), so that no record is
 // streamed by more than one compute unit at a time; while one wave of a SIMD
@@ -1366,12 +1366,13 @@ struct SegBufs {
     float *mapn;  // [segments, H, d_k, d_v] N of middle segments
 };
 
-// One workgroup per (segment, head), (d_k + d_v) / 16 waves of 16 columns: the
-// first d_k / 16 waves carry M (from the identity, V = 0) of a middle segment and
-// idle on segment 0, and issue all the chunk copies (their products are the
-// lighter ones: letting every wave copy makes the pass slower); the others carry
-// N (from zero), or on segment 0 the state from the initial state.
-constexpr int kSegNB = 1;  // 16-column blocks per wave in the map pass
+// One workgroup per (segment, head), (d_k + d_v) / 32 waves of 32 columns (two
+// 16-column blocks, so that every fragment read from LDS serves both): the first
+// d_k / 32 waves carry M (from the identity, V = 0) of a middle segment and idle on
+// segment 0, and issue all the chunk copies (their products are the lighter ones:
+// letting every wave copy makes the pass slower); the others carry N (from zero), or
+// on segment 0 the state from the initial state.
+constexpr int kSegNB = 2;  // 16-column blocks per wave in the map pass
 template <int K, int V>
 __global__ __launch_bounds__(64 * (K + V) / (16 * kSegNB)) void seg_kernel(PrefillArgs a, const int32_t *off,
                                                                            const int32_t *soff, int L,
