@@ -139,6 +139,21 @@ def test_prefill_segmented_state_pass(seg, monkeypatch):
     assert torch.equal(o1, o2) and torch.equal(s1, st)
 
 
+@pytest.mark.parametrize("dt,seg", [("bf16", None), ("bf16", "2"), ("f32", None)])
+def test_prefill_many_sequences(dt, seg, monkeypatch):
+    """700 packed sequences of 0 to 200 tokens, about a fifth of them empty: the chunk
+    and segment offsets span three 256-sequence blocks of their scan, every work item
+    finds its sequence by binary search over them, and with 2-chunk segments most
+    sequences of more than two chunks are cut; half the sequences start from zero."""
+    if seg is None:
+        monkeypatch.delenv("KDA_SEG_CHUNKS", raising=False)
+    else:
+        monkeypatch.setenv("KDA_SEG_CHUNKS", seg)
+    rng = np.random.default_rng(15)
+    lens = [0 if rng.random() < 0.2 else int(rng.integers(1, 201)) for _ in range(700)]
+    _prefill_case(inputs.prefill_inputs(15, lens, 2, 64, 64, dt, 0.1, "odd_zero"))
+
+
 @pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64), (64, 64)])
 def test_prefill_segmented_head_dims(dk, dv, monkeypatch):
     monkeypatch.setenv("KDA_SEG_CHUNKS", "2")
