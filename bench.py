@@ -194,8 +194,41 @@ def cpu_baseline_decode(d, target_s=5.0):
                        f"{el:.2f} s", seconds=el)
 
 
-def time_prefill_workload(name, steps, warmup, dev, stream):
-    """Median time of kda_chunk_fwd on a named synthetic workload (inputs resident on the device)."""
+def oracle_sample_parity(d, o, sT, seqs, heads):
+    """The CPU baseline on a sample of a workload: the fp64 oracle on sequences `seqs`
+    and heads `heads` of the device inputs d (timed, on the host's threads), and the
+    error of the GPU outputs o (bf16) and final states sT on the same sample."""
+    import numpy as np
+    import torch
+    import oracle
+    threads = _cpu_threads()
+    cu = d["cu_seqlens"].cpu().numpy().astype(np.int64)
+    tok = np.concatenate([np.arange(cu[n], cu[n + 1]) for n in seqs]).astype(np.int64)
+    tok_t = torch.from_numpy(tok).to(d["q"].device)
+    hd = torch.tensor(heads, device=d["q"].device)
+    sq = torch.tensor(seqs, device=d["q"].device)
+
+    def sub(x):
+        return x.index_select(0, tok_t).index_select(1, hd).float().cpu().numpy()
+
+    lens = [int(cu[n + 1] - cu[n]) for n in seqs]
+    cu_sub = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    s0 = d["initial_state"]
+    s0_sub = None if s0 is None else s0.index_select(0, sq).index_select(1, hd).cpu().numpy()
+    t0 = time.perf_counter()
+    ro, rs = oracle.prefill(sub(d["q"]), sub(d["k"]), sub(d["v"]), sub(d["log_alpha"]), sub(d["beta"]), cu_sub, 1.0,
+                            s0_sub, nthreads=threads)
+    elapsed = time.perf_counter() - t0
+    go, gs = sub(o), sT.index_select(0, sq).index_select(1, hd).cpu().numpy()
+    return {"o_err_over_rms": round(err_over_rms(go, ro, True), 6),
+            "final_state_err_over_rms": round(err_over_rms(gs, rs, False), 6), "tol": 2e-2,
+            "oracle_seconds": round(elapsed, 2), "cores": threads}
+
+
+def time_prefill_workload(name, steps, warmup, dev, stream, check=None):
+    """Median time of kda_chunk_fwd on a named synthetic workload (inputs resident on the
+    device); with check(lengths) -> (sequences, heads, description), also the last timed
+    call's outputs on that sample against the fp64 oracle."""
     import torch
     from gated_delta_rule_10_amd import inputs, kda
 
@@ -215,12 +248,18 @@ def time_prefill_workload(name, steps, warmup, dev, stream):
                           initial_state=d1["initial_state"], final_state=s1, o=o1, workspace=ws1, stream=stream)
 
     ms1 = time_calls(call, steps, warmup, stream)
+    torch.cuda.synchronize()
     b1 = prefill_bytes(T1, H1, K1, V1, N1, s0=d1["initial_state"] is not None)
     g1 = b1 / (ms1 / 1e3) / 1e9
     lens = d1["cu_seqlens"].diff().tolist()
+    par = None
+    if check is not None:
+        seqs, heads, what = check(lens)
+        par = oracle_sample_parity(d1, o1, s1, seqs, heads)
+        par["sample"] = what + ": the timed calls' outputs against the fp64 oracle (bf16 o: error beyond half a bf16 ulp)"
     del d1, o1, s1, ws1
     torch.cuda.empty_cache()
-    return {
+    return par, {
         "entry": "kda_chunk_fwd",
         "workload": f"{name}: {N1} sequence(s), {T1} tokens (lengths {min(lens)}-{max(lens)}), H={H1}, "
                     f"d_k={K1}, d_v={V1}, bf16, log alpha = -{w['decay_scale']} softplus(x), "
@@ -373,9 +412,23 @@ def main():
     # ---- the same operator on the other prefill workloads: one 1,048,576-token
     # sequence (the pages' 1M point), 16 packed sequences of mixed lengths, and
     # 4 x 4,096 tokens at H = 16
+    # (with the CPU baseline, each also checked against the oracle on a sample: heads 0
+    # and 31 of the 1M-token sequence; the shortest and longest of the 16 sequences on
+    # all 32 heads)
+    import numpy as np
+    checks = {
+        "long_1m": lambda lens: ([0], [0, 31], "heads 0 and 31 of the 1,048,576-token sequence"),
+        "varlen_512k": lambda lens: (sorted({int(np.argmin(lens)), int(np.argmax(lens))}), list(range(32)),
+                                     f"the shortest ({min(lens)} tokens) and longest ({max(lens)} tokens) "
+                                     "sequences, all 32 heads"),
+    }
+    sample_parity = {}
     if not args.no_variants:
         for wname, wsteps, wwarm in (("long_1m", 3, 1), ("varlen_512k", 5, 2), ("mid_4x4k", 20, 3)):
-            result["variants"][wname] = time_prefill_workload(wname, wsteps, wwarm, dev, stream)
+            chk = None if args.no_cpu_baseline else checks.get(wname)
+            par, result["variants"][wname] = time_prefill_workload(wname, wsteps, wwarm, dev, stream, chk)
+            if par is not None:
+                sample_parity[wname] = par
 
     # ---- decode: 64 sequences x 32 heads, fp32 cache -----------------------
     # The figure of record reads the state from HBM: four independent 128 MiB
@@ -498,6 +551,8 @@ def main():
                 "final_state_err_over_rms": round(err_over_rms(cpu_d["gpu_s"].numpy(), ref[1], False), 6),
                 "tol": 2e-2, "sample": "the timed calls' outputs, all 32 heads and 131072 tokens, against the "
                                       "fp64 oracle of the CPU baseline (bf16 o: error beyond half a bf16 ulp)"}
+    if sample_parity:
+        result.setdefault("parity", {})["workloads"] = sample_parity
     result["source_sha256"] = source_hash()  # the hash the profiles under profiles/ record
     print(json.dumps(result), flush=True)
 
