@@ -19,12 +19,13 @@
 //  * prep (persistent, all (chunk, head) items in parallel): every quantity that
 //    does not depend on the state. The 64x64 pairwise matrices are built from
 //    16-token sub-chunks: for a row in sub-chunk i and a column in sub-chunk
-//    j <= i, e^{G_r-G_s} = e^{G_r-G_b} e^{G_b-G_s} with b the last token before
-//    sub-chunk i, so every factor is <= 1 except, on the diagonal sub-chunk,
-//    e^{G_b-G_s} <= e^{(decay over 16 tokens)}. Those products run as fp16
-//    16x16x32 MFMAs with fp32 accumulation. Sub-chunks whose decay in some
-//    channel exceeds e^10 over 16 tokens take an exact fp32 per-element path
-//    for their diagonal block instead. T is inverted in fp32 (forward
+//    j <= i, e^{G_r-G_s} = e^{G_r-G_m} e^{G_m-G_s} with m after the 8th token of
+//    sub-chunk i, so every column factor below the diagonal is <= 1 and, on the
+//    diagonal, each factor is at most the decay over half a sub-chunk. Those
+//    products run as fp16 16x16x32 MFMAs with fp32 accumulation. Sub-chunks whose
+//    decay in some channel exceeds e^10 over 16 tokens, or whose operands would
+//    leave the fp16 range, take an exact fp32 per-element path for their diagonal
+//    block instead. T is inverted in fp32 (forward
 //    substitution on the 16x16 diagonal blocks, fp32 MFMA block recurrence
 //    below them); Y and P B are fp16 MFMA products of T Diag(beta) with the
 //    decayed keys and with P. Results are written to the workspace as fp16 MFMA
@@ -32,7 +33,8 @@
 //  * state passes over segments of consecutive chunks (see below): a map pass,
 //    a prefix over segments and an output pass. The state lives in MFMA
 //    accumulators (fp32); every value-side operand (state, X = V - K S) is
-//    scaled per value column by a power of two before its fp16 conversion, so
+//    scaled per value column by a power of two for its fp16 conversion (the
+//    state is held scaled, its scale changed only when its range requires), so
 //    the fp16 range never limits the magnitude of v or of the state.
 //
 // Options of kda_chunk_fwd_ex: the gates from bf16 pre-activations are formed
@@ -758,11 +760,11 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
 //    the last segment of a sequence writes the final state.
 // A workgroup covers all columns of one (segment, head) state (and of M); each
 // wave holds d_k rows of 32 columns (map pass) or 16 (output pass) in MFMA
-// accumulators, two waves per SIMD. A chunk's record is copied global -> LDS once per workgroup with
-// direct-to-LDS loads, one chunk ahead, into a two-buffer ring (the output pass
-// starts K.e^G and Q.e^G of the chunk after next too), so that no record is
-// streamed by more than one compute unit at a time; while one wave of a SIMD
-// waits on the memory pipeline the other computes.
+// accumulators, two waves per SIMD. A chunk's record is copied global -> LDS once
+// per workgroup with direct-to-LDS loads, one chunk ahead, into a two-buffer ring
+// (the output pass starts K.e^G and Q.e^G of the chunk after next too), so that no
+// record is streamed by more than one compute unit at a time; while one wave of a
+// SIMD waits on the memory pipeline the other computes.
 
 typedef __attribute__((address_space(3))) void lds_void;
 
