@@ -904,9 +904,16 @@ __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F);
 // rows 16 ct + 4g + e of column col0 + 16 j + r, held as S / sc[j] with a power of
 // two sc[j] per column (ChunkScale) that changes only when the held values leave the
 // range of their fp16 conversion. part_a: (K.e^G) S and (OUT) (Q.e^G) S, and
-// X = V - (K.e^G) S as a scaled fp16 operand (V = 0 without HASV). part_b: the state
+// X = V - (K.e^G) S as an fp16 operand (V = 0 without HASV); part_b: the state
 // update S <- Diag(e^{G_n}) S + Y^T X and (OUT) the outputs O = (Q.e^G) S + (P B) X of
 // tokens 16i + 4g + e in out[j][i].
+// X is held in the state's own scale when every column of the wave has X / sc below
+// 2^15 and its largest magnitude at least 2^-3 (or zero): then its elements carry an
+// error of at most 2^-12 of that largest magnitude, as in its own scale, and the
+// update and the outputs need no factor between the two scales (the decayed state is
+// the accumulator of the update's MFMAs, (Q.e^G) S that of the outputs'). Otherwise
+// (a wave-uniform branch) X takes its own power-of-two scale sigx: the relevant size
+// of X is then its own, since a strong decay leaves little of the state beside it.
 template <int NB>
 struct ChunkScale {
     float sc[NB], isc[NB];  // sc and 1 / sc, both powers of two
@@ -919,9 +926,14 @@ template <int K, int V, int NB, bool OUT, bool HASV>
 struct ChunkStep {
     static constexpr int NCB = K / 32, NCT = K / 16;
     using R = Rec<K>;
-    float sigs[NB], sigx[NB], ix[NB];  // ix = 1 / sigx
+    float sigs[NB], sigx[NB], ix[NB];  // with own_x: X held as X / sigx, ix = 1 / sigx
+    bool own_x;
     half8 xf[NB][2];
     f4 oa[NB][4];
+
+    static __device__ __forceinline__ float vval(const char *buf, int t, int col) {
+        return bf16_to_f32(*reinterpret_cast<const bf16_t *>(buf + ScanBuf<K, V>::VT + VTile<V>::off(t, col)));
+    }
 
     // The held values are the fp16 operand itself while every column's largest magnitude
     // lies in [2^-13, 2^15): below 2^-14 an element is subnormal in fp16, and its absolute
@@ -992,37 +1004,111 @@ struct ChunkStep {
                     for (int j = 0; j < NB; ++j) oa[j][i] = mfma(qx, sf[j][kb], oa[j][i]);
                 }
             }
+        // X / sc = V / sc - (K.e^G)(S / sc)
+        f4 X[NB][4];
+        bool held = true;
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-            f4 X[4];
-            float mx = 0.f;
+            float mj = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    float vv = 0.f;
-                    if (HASV)
-                        vv = bf16_to_f32(*reinterpret_cast<const bf16_t *>(
-                            buf + ScanBuf<K, V>::VT + VTile<V>::off(16 * i + 4 * g + e, col0 + 16 * j + r)));
-                    X[i][e] = fmaf(-sigs[j], xa[j][i][e], vv);
-                    mx = fmaxf(mx, fabsf(X[i][e]));
+                    // without V, X / sc = -xa: the sign goes onto the packed fp16 operand
+                    float xv = xa[j][i][e];
+                    if (HASV) xv = fmaf(vval(buf, 16 * i + 4 * g + e, col0 + 16 * j + r), cs.isc[j], -xv);
+                    X[j][i][e] = xv;
+                    mj = fmaxf(mj, fabsf(xv));
                 }
+            const float mx = col_max(mj);
+            held = held && mx < 0x1p15f && (mx >= 0x1p-3f || mx == 0.f);
+        }
+        own_x = __builtin_amdgcn_ballot_w64(!held) != 0;
+        if (own_x) {
+            // X in true units, then its own scale. X / sc is not finite only where V / sc
+            // passed 2^128: |(K.e^G)(S / sc)| < 2^38 (fp16 operands, d_k <= 128), so there
+            // V exceeds sc (K.e^G)(S / sc) by more than 2^90 and X = V in fp32.
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                float mt = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float xt = X[j][i][e] * cs.sc[j];
+                        if (HASV && !(fabsf(X[j][i][e]) <= 0x1.fffffep127f))
+                            xt = vval(buf, 16 * i + 4 * g + e, col0 + 16 * j + r);
+                        X[j][i][e] = xt;
+                        mt = fmaxf(mt, fabsf(xt));
+                    }
+                float invx;
+                sigx[j] = col_scale(col_max(mt), invx);
+                ix[j] = invx;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) X[j][i][e] *= invx;
             }
-            float invx;
-            sigx[j] = col_scale(col_max(mx), invx);
-            ix[j] = invx;
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    xf[j][ks][e] = static_cast<_Float16>(X[2 * ks][e] * invx);
-                    xf[j][ks][4 + e] = static_cast<_Float16>(X[2 * ks + 1][e] * invx);
+                    xf[j][ks][e] = static_cast<_Float16>(X[j][2 * ks][e]);
+                    xf[j][ks][4 + e] = static_cast<_Float16>(X[j][2 * ks + 1][e]);
+                }
+        if (!HASV) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    u4 w = __builtin_bit_cast(u4, xf[j][ks]);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) w[q] ^= 0x80008000u;
+                    xf[j][ks] = __builtin_bit_cast(half8, w);
                 }
         }
     }
 
     __device__ __forceinline__ void part_b(const char *buf, lds_cchar *fb, f4 (&S)[NB][NCT], ChunkScale<NB> &cs,
                                            f4 (&out)[NB][4], float scale, int g) {
+        if (!own_x) {
+            // S / sc <- Diag(e^{G_n}) (S / sc) + Y^T (X / sc): the decayed state is the
+            // accumulator of the two MFMAs
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const f4 gm = *reinterpret_cast<const f4 *>(buf + R::GAM + (16 * ct + 4 * g) * 4);
+                const half8 y0 = lds_frag(fb, R::YT + (ct * 2 + 0) * 1024);
+                const half8 y1 = lds_frag(fb, R::YT + (ct * 2 + 1) * 1024);
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    f4 d;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) d[e] = S[j][ct][e] * gm[e];
+                    S[j][ct] = mfma(y1, xf[j][1], mfma(y0, xf[j][0], d));
+                }
+            }
+            if (OUT) {
+                // O = sc ((Q.e^G)(S / sc) + (P B)(X / sc))
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const half8 p0 = lds_frag(fb, R::PB + tri(i, 0) * 1024);
+                    half8 p1 = p0;
+                    if (i >= 2) p1 = lds_frag(fb, R::PB + tri(i, 1) * 1024);
+#pragma unroll
+                    for (int j = 0; j < NB; ++j) {
+                        f4 px = mfma(p0, xf[j][0], oa[j][i]);
+                        if (i >= 2) px = mfma(p1, xf[j][1], px);
+                        const float os = sigs[j] * scale;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) out[j][i][e] = px[e] * os;
+                    }
+                }
+            }
+            return;
+        }
         // S <- Diag(e^{G_n}) S + Y^T X  (X held as X / sigx, S as S / sc). An update more
         // than 2^100 times the held state's scale restarts that column's scale at sigx (the
         // state is then negligible beside it), so that sigx / sc stays finite.
