@@ -137,8 +137,10 @@ __host__ __device__ __forceinline__ size_t a_nc(const PrefillArgs &a) {
 
 // ---------------------------------------------------------------------------
 // chunk and segment offsets: off[n] = sum_{m<n} ceil(len_m / 64), off[N] = total
-// chunks; soff[n] = sum_{m<n} G_m with G_m = max(1, ceil(chunks_m / L)) segments
-__global__ __launch_bounds__(256) void chunk_offsets_kernel(const int32_t *cu, int32_t N, int32_t L,
+// chunks; soff[n] = sum_{m<n} G_m segments. A sequence of at most L chunks is one
+// segment; a longer one has a segment 0 of L0 <= L chunks and then segments of L
+// chunks (the last one shorter): G = 1 + ceil((chunks - L0) / L).
+__global__ __launch_bounds__(256) void chunk_offsets_kernel(const int32_t *cu, int32_t N, int32_t L, int32_t L0,
                                                              int32_t *off, int32_t *soff) {
     __shared__ int32_t buf[2][256];
     __shared__ int32_t carry[2];
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(256) void chunk_offsets_kernel(const int32_t *cu, i
         int nc = 0, ns = 0;
         if (n < N) {
             nc = (max(cu[n + 1] - cu[n], 0) + kC - 1) / kC;
-            ns = max(1, (nc + L - 1) / L);
+            ns = nc <= L ? 1 : 1 + (nc - L0 + L - 1) / L;
         }
         buf[0][t] = nc;
         buf[1][t] = ns;
@@ -1437,6 +1439,21 @@ __device__ __forceinline__ SegInfo seg_of(const int32_t *soff, int N, int s) {
     return SegInfo{lo, s - soff[lo], soff[lo + 1] - soff[lo]};
 }
 
+// chunks [cb, ce) of a segment and its first token (the plan of chunk_offsets_kernel)
+struct SegRange {
+    int cb, ce, tbeg;
+};
+__device__ __forceinline__ SegRange seg_range(const PrefillArgs &a, const int32_t *off, const SegInfo &si, int L,
+                                              int L0) {
+    const int c0 = off[si.n], c1 = off[si.n + 1];
+    int cb = c0, ce = c1;
+    if (si.G > 1) {
+        cb = si.gl == 0 ? c0 : c0 + L0 + (si.gl - 1) * L;
+        ce = min(c1, si.gl == 0 ? c0 + L0 : cb + L);
+    }
+    return SegRange{cb, ce, a.cu_seqlens[si.n] + (cb - c0) * kC};
+}
+
 // initial / final state of sequence n, head h: [N, H, d_k, d_v] arrays, or slot
 // caches when slots are given (a negative slot: zero initial state, no final state)
 __device__ __forceinline__ const float *state_in(const PrefillArgs &a, int n, int h) {
@@ -1460,12 +1477,18 @@ struct SegBufs {
 // segment 0, and issue all the chunk copies (their products are the lighter ones:
 // letting every wave copy makes the pass slower); the others carry N (from zero), or
 // on segment 0 the state from the initial state.
+// With d_k = d_v (SEG0OUT), segment 0 is shorter than the others and its workgroup
+// runs the output pass of segment 0 instead (the workgroup then has the output
+// pass's d_v / 16 waves): its incoming state is known, so its outputs need not wait
+// for the prefix, and the output pass that follows has one segment fewer per
+// sequence. Its end state is the incoming state of segment 1 either way.
 constexpr int kSegNB = 2;  // 16-column blocks per wave in the map pass
-template <int K, int V>
+template <int K, int V, typename TOut, bool EPI>
 __global__ __launch_bounds__(64 * (K + V) / (16 * kSegNB)) void seg_kernel(PrefillArgs a, const int32_t *off,
-                                                                           const int32_t *soff, int L,
+                                                                           const int32_t *soff, int L, int L0,
                                                                            const char *recs, SegBufs sb) {
     constexpr int NB = kSegNB, NW = (K + V) / (16 * NB), WM = K / (16 * NB);
+    constexpr bool SEG0OUT = K == V;
     __shared__ __attribute__((aligned(16))) char lb0[ScanBuf<K, V>::BYTES];
     __shared__ __attribute__((aligned(16))) char lb1[ScanBuf<K, V>::BYTES];
     const int H = a.H;
@@ -1475,11 +1498,27 @@ __global__ __launch_bounds__(64 * (K + V) / (16 * kSegNB)) void seg_kernel(Prefi
     if (si.gl >= si.G - 1) return;    // the last segment has no successor
     const int tid = threadIdx.x, l = tid & 63, r = l & 15, g = l >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int cb = off[si.n] + si.gl * L, ce = min(off[si.n + 1], cb + L);
-    const int tbeg = a.cu_seqlens[si.n] + si.gl * L * kC, tend = a.cu_seqlens[si.n + 1];
+    const SegRange sr = seg_range(a, off, si, L, L0);
+    const int tend = a.cu_seqlens[si.n + 1];
     const char *hrec = recs + static_cast<size_t>(h) * a_nc(a) * Rec<K>::BYTES;
     const bf16_t *vg = static_cast<const bf16_t *>(a.v);
     const size_t skv = (static_cast<size_t>(s) * H + h) * K * V;
+    if constexpr (SEG0OUT) {
+        if (si.gl == 0) {
+            constexpr int OW = V / 16;
+            static_assert(OW == NW, "the output pass's waves are the map pass's");
+            static_assert(static_cast<size_t>(kC) * V * 4 <= Rec<K>::YT, "the fp32 epilogue tile fits a buffer");
+            f4 S1[1][K / 16];
+            const int col0 = 16 * w;
+            load_state<K, 1>(S1, state_in(a, si.n, h), V, col0, r, g);
+            const Epi ep{static_cast<const bf16_t *>(a.z), a.nw, a.eps, a.norm, a.zact};
+            run_segment<K, V, 1, true, true, true, OW, OW, EPI, TOut>(lb0, lb1, nullptr, S1, hrec, sr.cb, sr.ce,
+                                                                      sr.tbeg, tend, vg, static_cast<TOut *>(a.o), H,
+                                                                      h, a.scale, ep, true, tid, w, l, r, g, col0);
+            store_state<K, 1>(S1, sb.sin + skv + static_cast<size_t>(H) * K * V, V, col0, r, g);
+            return;
+        }
+    }
     f4 S[NB][K / 16];
     if (w < WM) {
         const int col0 = 16 * NB * w;
@@ -1489,27 +1528,27 @@ __global__ __launch_bounds__(64 * (K + V) / (16 * kSegNB)) void seg_kernel(Prefi
             for (int ct = 0; ct < K / 16; ++ct)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) S[j][ct][e] = (16 * ct + 4 * g + e == col0 + 16 * j + r) ? 1.f : 0.f;
-        run_segment<K, V, NB, false, false, true, NW, WM, false, float>(lb0, lb1, nullptr, S, hrec, cb, ce, tbeg,
-                                                                        tend, vg, nullptr, H, h, 1.f, Epi{},
+        run_segment<K, V, NB, false, false, true, NW, WM, false, float>(lb0, lb1, nullptr, S, hrec, sr.cb, sr.ce,
+                                                                        sr.tbeg, tend, vg, nullptr, H, h, 1.f, Epi{},
                                                                         si.gl > 0, tid, w, l, r, g, col0);
         if (si.gl > 0) store_state<K, NB>(S, sb.mapm + (static_cast<size_t>(s) * H + h) * K * K, K, col0, r, g);
     } else {
         const int col0 = 16 * NB * (w - WM);
         const float *init = si.gl == 0 ? state_in(a, si.n, h) : nullptr;
         load_state<K, NB>(S, init, V, col0, r, g);
-        run_segment<K, V, NB, false, true, true, NW, WM, false, float>(lb0, lb1, nullptr, S, hrec, cb, ce, tbeg, tend,
-                                                                       vg, nullptr, H, h, 1.f, Epi{}, true, tid, w,
-                                                                       l, r, g, col0);
+        run_segment<K, V, NB, false, true, true, NW, WM, false, float>(lb0, lb1, nullptr, S, hrec, sr.cb, sr.ce,
+                                                                       sr.tbeg, tend, vg, nullptr, H, h, 1.f, Epi{},
+                                                                       true, tid, w, l, r, g, col0);
         store_state<K, NB>(S, si.gl == 0 ? sb.sin + skv + static_cast<size_t>(H) * K * V : sb.mapn + skv, V, col0, r,
                            g);
     }
 }
 
-// For a sequence cut into several segments: a copy of its initial state (zeros
-// without one) as the incoming state of its segment 0, which the output pass
-// reads. The output pass writes final states (which may alias the initial
-// states) while other segments of it still run, and its segment-0 workgroups may
-// run beside the map pass, so they read this copy.
+// For a sequence cut into several segments when d_k != d_v (segment 0 then goes
+// through the output pass): a copy of its initial state (zeros without one) as the
+// incoming state of its segment 0, which the output pass reads. The output pass
+// writes final states (which may alias the initial states) while other segments of
+// it still run, so segment 0 reads this copy.
 // Each state is copied by kSeedParts workgroups, so that a few long sequences still
 // spread the copies over many compute units.
 constexpr int kSeedParts = 16;
@@ -1599,7 +1638,7 @@ __global__ __launch_bounds__(64 * K / 16) void prefix_kernel(const int32_t *soff
 
 template <int K, int V, typename TOut, bool EPI>
 __global__ __launch_bounds__(64 * V / 16) void out_kernel(PrefillArgs a, const int32_t *off, const int32_t *soff,
-                                                          int L, const char *recs, SegBufs sb) {
+                                                          int L, int L0, const char *recs, SegBufs sb) {
     constexpr int NB = 1, NW = V / 16;
     // the fp32 epilogue tile goes into the K.e^G / Q.e^G region of a chunk buffer when it fits
     constexpr bool FTD = EPI && static_cast<size_t>(kC) * V * 4 > Rec<K>::YT;
@@ -1610,11 +1649,12 @@ __global__ __launch_bounds__(64 * V / 16) void out_kernel(PrefillArgs a, const i
     const int s = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
     if (s >= soff[a.N]) return;
     const SegInfo si = seg_of(soff, a.N, s);
+    if (K == V && si.G > 1 && si.gl == 0) return;  // segment 0's outputs came from the map pass
     const int tid = threadIdx.x, l = tid & 63, r = l & 15, g = l >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col0 = 16 * NB * w;
-    const int cb = off[si.n] + si.gl * L, ce = min(off[si.n + 1], cb + L);
-    const int tbeg = a.cu_seqlens[si.n] + si.gl * L * kC, tend = a.cu_seqlens[si.n + 1];
+    const SegRange sr = seg_range(a, off, si, L, L0);
+    const int cb = sr.cb, ce = sr.ce, tbeg = sr.tbeg, tend = a.cu_seqlens[si.n + 1];
     f4 S[NB][K / 16];
     const float *init = si.G == 1 ? state_in(a, si.n, h) : sb.sin + (static_cast<size_t>(s) * H + h) * K * V;
     load_state<K, NB>(S, init, V, col0, r, g);
@@ -1642,26 +1682,38 @@ int cu_count() {
     return n;
 }
 
+// Segment plan. With d_k = d_v the map pass also runs the output pass of each
+// sequence's segment 0 (seg_kernel), at about 0.6 of the map pass's rate per chunk
+// (4.2 against 2.6 us per chunk at 128K tokens), so segment 0 gets 5/8 of the
+// others' L chunks and both passes then take about L chunks' time.
+constexpr int kSeg0Eighths = 5;
+int seg0_chunks(int L, bool seg0out) { return seg0out ? std::max(1, kSeg0Eighths * L / 8) : L; }
+
 // Chunks per segment: enough segments to give every compute unit a (segment,
-// head) at this size, and at least 16 chunks each. KDA_SEG_CHUNKS overrides it
-// (tests of the segment bookkeeping at small sizes), up to the chunk count.
-int seg_chunks(int32_t N, int32_t T, int32_t H) {
+// head) in each state pass for one long sequence at this size (with segment 0
+// counted at its shorter length), and at least 16 chunks each. KDA_SEG_CHUNKS
+// overrides it (tests of the segment bookkeeping at small sizes), up to the chunk count.
+int seg_chunks(int32_t N, int32_t T, int32_t H, bool seg0out) {
     const int64_t nc = (static_cast<int64_t>(T) + kC - 1) / kC + N;
     if (const char *e = std::getenv("KDA_SEG_CHUNKS")) {
         const int v = std::atoi(e);
         if (v >= 1) return static_cast<int>(std::min<int64_t>(v, nc));
     }
-    return static_cast<int>(std::max<int64_t>(16, (nc * H + 255) / 256));
+    // (G - 1) segments of L and one of 5 L / 8 per long sequence, G - 1 = 256 / H
+    const int64_t den = 8 * 256 + (seg0out ? kSeg0Eighths * static_cast<int64_t>(H) : 0);
+    return static_cast<int>(std::max<int64_t>(16, (8 * nc * H + den - 1) / den));
 }
 
 template <int K, int V>
 struct WsLayout {
-    int L;
+    int L, L0;
     size_t nc, nseg, off, soff, recs, sin, mapn, mapm, bytes;
     WsLayout(int32_t N, int32_t T, int32_t H) {
-        L = seg_chunks(N, T, H);
+        L = seg_chunks(N, T, H, K == V);
+        L0 = seg0_chunks(L, K == V);
         nc = static_cast<size_t>((static_cast<int64_t>(T) + kC - 1) / kC) + N;
-        nseg = (nc + L - 1) / L + N;
+        // sum over sequences of ceil(chunks / L), plus one for each sequence longer than L
+        nseg = (nc + L - 1) / L + N + std::min<size_t>(N, (nc + L - 1) / L);
         off = 0;
         soff = align256(static_cast<size_t>(N + 1) * 4);
         recs = soff + align256(static_cast<size_t>(N + 1) * 4);
@@ -1673,16 +1725,37 @@ struct WsLayout {
 };
 
 template <int K, int V>
-hipError_t launch_out(const PrefillArgs &a, const int32_t *off, const int32_t *soff, int L, const char *recs,
+hipError_t launch_out(const PrefillArgs &a, const int32_t *off, const int32_t *soff, int L, int L0, const char *recs,
                       const SegBufs &sb, size_t units, hipStream_t st) {
     const dim3 og(static_cast<unsigned>(units)), ob(64 * V / 16);
     const bool epi = a.norm || a.z;
     if (a.out_dtype == KDA_BF16) {
-        if (epi) hipLaunchKernelGGL((out_kernel<K, V, bf16_t, true>), og, ob, 0, st, a, off, soff, L, recs, sb);
-        else hipLaunchKernelGGL((out_kernel<K, V, bf16_t, false>), og, ob, 0, st, a, off, soff, L, recs, sb);
+        if (epi) hipLaunchKernelGGL((out_kernel<K, V, bf16_t, true>), og, ob, 0, st, a, off, soff, L, L0, recs, sb);
+        else hipLaunchKernelGGL((out_kernel<K, V, bf16_t, false>), og, ob, 0, st, a, off, soff, L, L0, recs, sb);
     } else {
-        if (epi) hipLaunchKernelGGL((out_kernel<K, V, float, true>), og, ob, 0, st, a, off, soff, L, recs, sb);
-        else hipLaunchKernelGGL((out_kernel<K, V, float, false>), og, ob, 0, st, a, off, soff, L, recs, sb);
+        if (epi) hipLaunchKernelGGL((out_kernel<K, V, float, true>), og, ob, 0, st, a, off, soff, L, L0, recs, sb);
+        else hipLaunchKernelGGL((out_kernel<K, V, float, false>), og, ob, 0, st, a, off, soff, L, L0, recs, sb);
+    }
+    return hipGetLastError();
+}
+
+// the map pass; with d_k = d_v it also writes segment 0's outputs (output type and epilogue)
+template <int K, int V>
+hipError_t launch_seg(const PrefillArgs &a, const int32_t *off, const int32_t *soff, int L, int L0, const char *recs,
+                      const SegBufs &sb, size_t units, hipStream_t st) {
+    const dim3 gg(static_cast<unsigned>(units)), gb(64 * (K + V) / (16 * kSegNB));
+    const bool epi = a.norm || a.z;
+    if constexpr (K == V) {
+        if (a.out_dtype == KDA_BF16) {
+            if (epi) hipLaunchKernelGGL((seg_kernel<K, V, bf16_t, true>), gg, gb, 0, st, a, off, soff, L, L0, recs, sb);
+            else hipLaunchKernelGGL((seg_kernel<K, V, bf16_t, false>), gg, gb, 0, st, a, off, soff, L, L0, recs, sb);
+        } else {
+            if (epi) hipLaunchKernelGGL((seg_kernel<K, V, float, true>), gg, gb, 0, st, a, off, soff, L, L0, recs, sb);
+            else hipLaunchKernelGGL((seg_kernel<K, V, float, false>), gg, gb, 0, st, a, off, soff, L, L0, recs, sb);
+        }
+    } else {
+        (void)epi;
+        hipLaunchKernelGGL((seg_kernel<K, V, float, false>), gg, gb, 0, st, a, off, soff, L, L0, recs, sb);
     }
     return hipGetLastError();
 }
@@ -1696,7 +1769,7 @@ hipError_t launch_kv(const PrefillArgs &a, hipStream_t st) {
     char *recs = ws + lay.recs;
     const SegBufs sb{reinterpret_cast<float *>(ws + lay.sin), reinterpret_cast<float *>(ws + lay.mapm),
                      reinterpret_cast<float *>(ws + lay.mapn)};
-    hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(256), 0, st, a.cu_seqlens, a.N, lay.L, off, soff);
+    hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(256), 0, st, a.cu_seqlens, a.N, lay.L, lay.L0, off, soff);
     if (a.T > 0) {
         const size_t items = lay.nc * a.H;
         const size_t wgs = std::min(items, static_cast<size_t>(kPrepWgsPerCu) * cu_count());
@@ -1710,16 +1783,17 @@ hipError_t launch_kv(const PrefillArgs &a, hipStream_t st) {
     // every sequence has at most ceil(T / 64) chunks: one segment if that fits in L
     const int64_t maxc = (static_cast<int64_t>(a.T) + kC - 1) / kC;
     const size_t units = lay.nseg * a.H;
-    if (maxc <= lay.L) return launch_out<K, V>(a, off, soff, lay.L, recs, sb, units, st);
+    if (maxc <= lay.L) return launch_out<K, V>(a, off, soff, lay.L, lay.L0, recs, sb, units, st);
 
-    hipLaunchKernelGGL((seed_kernel<K, V>), dim3(static_cast<unsigned>(a.N) * a.H * kSeedParts), dim3(256), 0, st, a,
-                       soff, sb);
-    hipLaunchKernelGGL((seg_kernel<K, V>), dim3(static_cast<unsigned>(units)), dim3(64 * (K + V) / (16 * kSegNB)), 0,
-                       st, a, off, soff, lay.L, recs, sb);
-    if (maxc > 2 * static_cast<int64_t>(lay.L))
+    if (K != V)
+        hipLaunchKernelGGL((seed_kernel<K, V>), dim3(static_cast<unsigned>(a.N) * a.H * kSeedParts), dim3(256), 0, st,
+                           a, soff, sb);
+    const hipError_t e = launch_seg<K, V>(a, off, soff, lay.L, lay.L0, recs, sb, units, st);
+    if (e != hipSuccess) return e;
+    if (maxc > static_cast<int64_t>(lay.L0) + lay.L)  // some sequence has three or more segments
         hipLaunchKernelGGL((prefix_kernel<K, V>), dim3(static_cast<unsigned>(a.N) * a.H * (V / 16)), dim3(64 * K / 16), 0, st,
                            soff, a.N, a.H, sb);
-    return launch_out<K, V>(a, off, soff, lay.L, recs, sb, units, st);
+    return launch_out<K, V>(a, off, soff, lay.L, lay.L0, recs, sb, units, st);
 }
 
 // Workspace of kda_chunk_fwd_ex_noalloc. In host code this name is the runtime's
