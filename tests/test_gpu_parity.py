@@ -231,8 +231,8 @@ def test_prefill_varlen_512k_sampled():
 def test_prefill_long_1m_sampled():
     """The pages' 1M-token point: one 1,048,576-token sequence, H=32, d=128,
     bf16, random initial state, in the library's own segment plan (16,384 chunks
-    per head in segments of 2,049, a 29 GB workspace): heads 0 and 31 computed
-    completely by the oracle."""
+    per head: a segment 0 of 1,187 chunks and 8 of up to 1,900, a 29 GB
+    workspace): heads 0 and 31 computed completely by the oracle."""
     d = inputs.device_workload_inputs("long_1m")
     assert d["q"].shape[0] == 1 << 20
     o, sT = gc.run_prefill(d)
