@@ -748,18 +748,19 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
 }
 
 // ---------------------------------------------------------------------------
-// State passes. The chunks of a sequence are cut into segments of L consecutive
-// chunks. Every chunk maps its incoming state affinely,
+// State passes. The chunks of a sequence are cut into segments of consecutive
+// chunks (a segment 0 of L0 chunks, then segments of L). Every chunk maps its
+// incoming state affinely,
 //   S <- (Diag(e^{G_n}) - Y^T (K.e^G)) S + Y^T V,
 // so a segment does too: S_out = M S_in + N, with M (d_k x d_k) the segment run
 // from the identity with V = 0 and N (d_k x d_v) the segment run from zero.
 //  * seg_kernel, every segment but the last of each sequence, in parallel:
-//    segment 0 runs from the initial state (its end state enters segment 1), a
-//    middle segment runs from the identity for M and from zero for N, both in
-//    one workgroup;
+//    segment 0 runs from the initial state (its end state enters segment 1; with
+//    d_k = d_v it also writes its outputs there), a middle segment runs from the
+//    identity for M and from zero for N, both in one workgroup;
 //  * prefix_kernel: S_in(g + 1) = M_g S_in(g) + N_g along the middle segments;
-//  * out_kernel, every segment in parallel from its incoming state, with outputs;
-//    the last segment of a sequence writes the final state.
+//  * out_kernel, every other segment in parallel from its incoming state, with
+//    outputs; the last segment of a sequence writes the final state.
 // A workgroup covers all columns of one (segment, head) state (and of M); each
 // wave holds d_k rows of 32 columns (map pass) or 16 (output pass) in MFMA
 // accumulators, two waves per SIMD. A chunk's record is copied global -> LDS once
@@ -1473,8 +1474,8 @@ struct SegBufs {
 
 // One workgroup per (segment, head), (d_k + d_v) / 32 waves of 32 columns (two
 // 16-column blocks, so that every fragment read from LDS serves both): the first
-// d_k / 32 waves carry M (from the identity, V = 0) of a middle segment and idle on
-// segment 0, and issue all the chunk copies (their products are the lighter ones:
+// d_k / 32 waves carry M (from the identity, V = 0) of a middle segment (and idle
+// on segment 0 when d_k != d_v), and issue all the chunk copies (their products are the lighter ones:
 // letting every wave copy makes the pass slower); the others carry N (from zero), or
 // on segment 0 the state from the initial state.
 // With d_k = d_v (SEG0OUT), segment 0 is shorter than the others and its workgroup

@@ -50,13 +50,16 @@
  *    conversion).
  *  - Test overrides, read from the environment: KDA_SEG_CHUNKS=n (at every
  *    call) cuts the state passes of the bf16 prefill into segments of n
- *    chunks (at most the chunk count), and KDA_PREFILL_KERNEL=valu (once per
- *    process) runs bf16 inputs through the fp32 prefill kernels. The workspace
- *    size depends on both: query it under the environment of the call.
+ *    chunks (at most the chunk count; with d_k = d_v a sequence's segment 0
+ *    has floor(5 n / 8) chunks, at least one), and KDA_PREFILL_KERNEL=valu
+ *    (once per process) runs bf16 inputs through the fp32 prefill kernels.
+ *    The workspace size depends on both: query it under the environment of
+ *    the call.
  *  - The library's only global state is a per-device cache of the compute
- *    unit count (atomic). Calls are thread-safe and take no lock; calls on
- *    different streams that write the same memory (outputs, states, a shared
- *    workspace) race.
+ *    unit count and of the address of kda_chunk_fwd_ex_noalloc's static
+ *    scratch (both atomic), and that scratch itself. Calls are thread-safe
+ *    and take no lock; calls on different streams that write the same memory
+ *    (outputs, states, a shared workspace) race.
  *  - No C++ exception crosses this interface.
  */
 #ifndef KDA_H_
