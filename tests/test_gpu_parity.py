@@ -154,6 +154,22 @@ def test_prefill_many_sequences(dt, seg, monkeypatch):
     _prefill_case(inputs.prefill_inputs(15, lens, 2, 64, 64, dt, 0.1, "odd_zero"))
 
 
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64)])
+def test_prefill_plan_boundaries(dk, dv, monkeypatch):
+    """Sequence lengths at the edges of the segment plan, with segments of 8 chunks
+    (KDA_SEG_CHUNKS=8) and, at d_k = d_v, a segment 0 of 5 that the map pass runs
+    with outputs: 8 chunks (one segment), 9 and 13 (segment 0 and one more, no
+    prefix step), 14 and 21 (three segments), 22 (four), each also one token short
+    and one token over, beside an empty and a one-token sequence. At d_k != d_v
+    every segment has 8 chunks and segment 0 goes through the output pass."""
+    monkeypatch.setenv("KDA_SEG_CHUNKS", "8")
+    lens = []
+    for c in (8, 9, 13, 14, 21, 22):
+        lens += [64 * c - 1, 64 * c, 64 * c + 1]
+    lens += [0, 1]
+    _prefill_case(inputs.prefill_inputs(16, lens, 2, dk, dv, "bf16", 0.1, "random"))
+
+
 @pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64), (64, 64)])
 def test_prefill_segmented_head_dims(dk, dv, monkeypatch):
     monkeypatch.setenv("KDA_SEG_CHUNKS", "2")
