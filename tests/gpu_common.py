@@ -109,6 +109,19 @@ def norm_epilogue_bound(pre, tol, norm_eps, weight=None, gate=None):
     return bound
 
 
+def gate_epilogue_bound(pre, tol, gate):
+    """Per-element error bound of an output gated without the norm, y_i = o_i act(z_i),
+    from the bar on o (every element within e = tol * RMS(o)): |dy_i| <= e |act(z_i)|.
+    The plain bar on y itself would instead be tol * RMS(y), about tol * RMS(o) * RMS(act(z)),
+    which an element with |act(z_i)| several times RMS(act(z)) exceeds whenever its o carries
+    an error near the bar. `pre` is the oracle's output before the gate, `gate` act(z)."""
+    pre = np.asarray(pre, np.float64)
+    if pre.size == 0:
+        return pre
+    e = tol * float(np.sqrt(np.mean(pre * pre)))
+    return e * np.abs(np.asarray(gate, np.float64))
+
+
 def assert_within_bound(name, got, ref, bound, bf16_rounded=False):
     """Every element within its own bound (after half a bf16 ulp for bf16 outputs)."""
     got = np.asarray(got, np.float64)

@@ -55,14 +55,17 @@ def _prefill_case(seed, lens, Hk, H, K, V, dt, *, gates="pre", norm=False, z_act
         ref_o, ref_s = oo.prefill_ex(x["q"], x["k"], x["v"], cu, initial_state=s0, **kw_o)
     tol = gc.TOL_BF16 if bf else gc.TOL_F32
     bound = None
-    if norm:  # the bar on the operator's o, carried through the row normalisation
+    if norm or z_act is not None:  # the bar on the operator's o, carried through the epilogue
         kw_pre = {k: v for k, v in kw_o.items() if k not in ("norm", "norm_eps", "norm_weight", "out_gate",
                                                               "out_gate_act")}
         init = cache if slots is not None else s0
         extra = dict(state_slots=s_np) if slots is not None else {}
         pre, _ = oo.prefill_ex(x["q"], x["k"], x["v"], cu, initial_state=init, **extra, **kw_pre)
         gate = None if z_act is None else oo.output_gate(np.ones_like(pre), x["out_gate"], z_act)
-        bound = gc.norm_epilogue_bound(pre, tol, 1e-5, x["norm_weight"], gate)
+        if norm:
+            bound = gc.norm_epilogue_bound(pre, tol, 1e-5, x["norm_weight"], gate)
+        else:
+            bound = gc.gate_epilogue_bound(pre, tol, gate)
     for od in (out_dtypes or ([torch.bfloat16, torch.float32] if bf else [torch.float32])):
         if slots is not None:
             st = torch.from_numpy(cache).cuda()
