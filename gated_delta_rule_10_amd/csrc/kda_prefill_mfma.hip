@@ -911,12 +911,13 @@ __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F);
 // update S <- Diag(e^{G_n}) S + Y^T X and (OUT) the outputs O = (Q.e^G) S + (P B) X of
 // tokens 16i + 4g + e in out[j][i].
 // X is held in the state's own scale when every column of the wave has X / sc below
-// 2^15 and its largest magnitude at least 2^-3 (or zero): then its elements carry an
-// error of at most 2^-12 of that largest magnitude, as in its own scale, and the
-// update and the outputs need no factor between the two scales (the decayed state is
-// the accumulator of the update's MFMAs, (Q.e^G) S that of the outputs'). Otherwise
-// (a wave-uniform branch) X takes its own power-of-two scale sigx: the relevant size
-// of X is then its own, since a strong decay leaves little of the state beside it.
+// 2^15 and its largest magnitude at least 2^-3 (or zero): then its fp16 elements carry
+// an error of at most half an fp16 ulp of that largest magnitude (subnormal ones far
+// less), as in a scale of its own, and the update and the outputs need no factor
+// between two scales (the decayed state is the accumulator of the update's MFMAs,
+// (Q.e^G) S that of the outputs'). Otherwise (a wave-uniform branch) X takes its own
+// power-of-two scale sigx: X's size beside the state does not bound its effect, since
+// a strong decay leaves little of the state beside the update.
 template <int NB>
 struct ChunkScale {
     float sc[NB], isc[NB];  // sc and 1 / sc, both powers of two
