@@ -205,6 +205,27 @@ def test_prefill_value_magnitudes(c, monkeypatch):
         gc.assert_close(f"final_state x {c:.1e}", gc.host(sT), ref_s * c, gc.TOL_BF16)
 
 
+@pytest.mark.parametrize("seg", [None, "2"])
+def test_prefill_tiny_state_large_values(seg, monkeypatch):
+    """An initial state of fp32 subnormals (about 2^-134) and v scaled by 2^20: the
+    state's held scale stops at its lower clamp, so V / sc passes the fp32 range and
+    the state passes take X in its own scale from V itself. The oracle runs on the
+    device tensors' exact values."""
+    if seg is None:
+        monkeypatch.delenv("KDA_SEG_CHUNKS", raising=False)
+    else:
+        monkeypatch.setenv("KDA_SEG_CHUNKS", seg)
+    inp = inputs.prefill_inputs(17, [300, 130], 2, 128, 128, "bf16", 0.1, "random")
+    d = gc.to_device(inp)
+    d = dict(d, v=d["v"] * 2.0 ** 20, initial_state=d["initial_state"] * 2.0 ** -128)
+    assert float(d["initial_state"].abs().max()) < 2.0 ** -126
+    ref_o, ref_s, _ = gc.oracle_prefill(d)
+    for od in (torch.bfloat16, torch.float32):
+        o, sT = gc.run_prefill(d, out_dtype=od)
+        gc.assert_close(f"o[{od}]", gc.host(o), ref_o, gc.TOL_BF16, bf16_rounded=od == torch.bfloat16)
+        gc.assert_close("final_state", gc.host(sT), ref_s, gc.TOL_BF16)
+
+
 def test_prefill_long_128k_sampled():
     """One 131072-token sequence, H=32, d=128, bf16, random initial state:
     heads 0 and 31 computed completely by the oracle, for bf16 outputs and for
