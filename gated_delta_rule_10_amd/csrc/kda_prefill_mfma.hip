@@ -1574,11 +1574,17 @@ __global__ __launch_bounds__(256) void seed_kernel(PrefillArgs a, const int32_t 
 // one step ahead, and the same rows of the tile (transposed in LDS) as B operands;
 // the accumulator starts from N_g. The steps are sequential, so the time per step
 // is one chain of K/4 MFMAs and one barrier.
+// Workgroups go to the 8 XCDs in turn (workgroup b to XCD b % 8), and the d_v / 16
+// tiles of one (sequence, head) all read its whole M_g at every step, so they are
+// placed on one XCD to share its L2: (sequence, head) u = 8 (b / 8 / NV) + b % 8,
+// tile (b / 8) % NV.
+constexpr int kXcds = 8;
 template <int K, int V>
 __global__ __launch_bounds__(64 * K / 16) void prefix_kernel(const int32_t *soff, int N, int H, SegBufs sb) {
     constexpr int NV = V / 16, KQ = K / 4, NT = 64 * K / 16;
     __shared__ __attribute__((aligned(16))) float xt[2][16][K + 4];  // the tile, [buffer][column][row]
-    const int b = blockIdx.x, vt = b % NV, nh = b / NV, n = nh / H, h = nh - (nh / H) * H;
+    const int b = blockIdx.x, xi = b / kXcds, vt = xi % NV, nh = (xi / NV) * kXcds + b % kXcds;
+    const int n = nh / H, h = nh - (nh / H) * H;
     if (n >= N) return;
     const int s0 = soff[n], G = soff[n + 1] - s0;
     if (G < 3) return;
@@ -1793,8 +1799,10 @@ hipError_t launch_kv(const PrefillArgs &a, hipStream_t st) {
     const hipError_t e = launch_seg<K, V>(a, off, soff, lay.L, lay.L0, recs, sb, units, st);
     if (e != hipSuccess) return e;
     if (maxc > static_cast<int64_t>(lay.L0) + lay.L)  // some sequence has three or more segments
-        hipLaunchKernelGGL((prefix_kernel<K, V>), dim3(static_cast<unsigned>(a.N) * a.H * (V / 16)), dim3(64 * K / 16), 0, st,
-                           soff, a.N, a.H, sb);
+        hipLaunchKernelGGL((prefix_kernel<K, V>),
+                           dim3(static_cast<unsigned>((static_cast<int64_t>(a.N) * a.H + kXcds - 1) / kXcds) * kXcds *
+                                (V / 16)),
+                           dim3(64 * K / 16), 0, st, soff, a.N, a.H, sb);
     return launch_out<K, V>(a, off, soff, lay.L, lay.L0, recs, sb, units, st);
 }
 
