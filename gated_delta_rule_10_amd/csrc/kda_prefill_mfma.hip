@@ -257,10 +257,19 @@ struct PrepRaw {
     // Loads are unconditional: a token past the sequence end reads token t0 of the chunk.
     // q and k come from key head h / (H / Hk) of the value head h.
     __device__ __forceinline__ void load(const PrefillArgs &a, const PrepItem &it, bool ok, int tr, int g) {
+        load_gates(a, it, ok, tr, g);
+        load_kq(a, it, tr, g);
+    }
+    // The next item's inputs load in two parts: its decay and beta once the current
+    // item's elementwise phase is done, its k and q one phase later (load_kq), once the
+    // pairwise products have consumed the current row operands. A single burst of all
+    // of them together with the current item's stores held the CU's memory pipeline
+    // (64 KB of loads and 32 KB of stores per workgroup): one part is 1.9 % faster per call.
+    __device__ __forceinline__ void load_gates(const PrefillArgs &a, const PrepItem &it, bool ok, int tr, int g) {
         valid = ok && tr < it.nt;
         const size_t t = static_cast<size_t>(it.t0 + (valid ? tr : 0));
         const size_t tok = t * a.H + it.h;
-        const size_t row = tok * K, rowk = (t * a.Hk + it.h / (a.H / a.Hk)) * K;
+        const size_t row = tok * K;
         const int o = 16 * (g & 1) + 8 * (g >> 1);
 #pragma unroll
         for (int cb = 0; cb < K / 32; ++cb) {
@@ -271,12 +280,22 @@ struct PrepRaw {
                 gv[cb][0] = *reinterpret_cast<const float4 *>(a.g + row + ch);
                 gv[cb][1] = *reinterpret_cast<const float4 *>(a.g + row + ch + 4);
             }
-            kv[cb] = *reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.k) + rowk + ch);
-            qv[cb] = *reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.q) + rowk + ch);
         }
         // raw bits: converting here would make the wave wait for the load at once
         if (a.by) betaw = static_cast<const bf16_t *>(a.by)[tok];
         else betaw = reinterpret_cast<const uint32_t *>(a.beta)[tok];
+    }
+    // k and q of an item (valid as set by load_gates for the same item)
+    __device__ __forceinline__ void load_kq(const PrefillArgs &a, const PrepItem &it, int tr, int g) {
+        const size_t t = static_cast<size_t>(it.t0 + (valid ? tr : 0));
+        const size_t rowk = (t * a.Hk + it.h / (a.H / a.Hk)) * K;
+        const int o = 16 * (g & 1) + 8 * (g >> 1);
+#pragma unroll
+        for (int cb = 0; cb < K / 32; ++cb) {
+            const int ch = 32 * cb + o;
+            kv[cb] = *reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.k) + rowk + ch);
+            qv[cb] = *reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.q) + rowk + ch);
+        }
     }
     // beta (sigmoid of the bf16 pre-activation when given), 0 past the sequence end
     __device__ __forceinline__ float beta(const PrefillArgs &a) const {
@@ -537,11 +556,11 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
         if (w + 2 < 4) sm.u.a.colv[vblk(w + 2, w)][cb][l] = cv2;
         if (w == 0) sm.u.a.colv[vblk(3, 0)][cb][l] = cv3;
     }
-    // the next item's inputs load from here on (k, q and the decay of this one are no longer held)
+    // the next item's decay and beta load from here on (this item's are no longer held)
     {
         const int un = u + static_cast<int>(gridDim.x);
         nx = prep_item(a, off, un < total ? un : 0);
-        raw.load(a, nx, un < total, tr, g);
+        raw.load_gates(a, nx, un < total, tr, g);
     }
     __syncthreads();
 
@@ -560,6 +579,7 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
             }
         }
     }
+    raw.load_kq(a, nx, tr, g);  // this item's row operands are consumed: the next item's k and q
     __syncthreads();  // the factors and colv are no longer read; the union now holds A, P, T
 
     // blocks j <= w of A (strictly lower on the diagonal) and P (lower); the T and P
