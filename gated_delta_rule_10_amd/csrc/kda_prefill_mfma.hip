@@ -260,11 +260,12 @@ struct PrepRaw {
         load_gates(a, it, ok, tr, g);
         load_kq(a, it, tr, g);
     }
-    // The next item's inputs load in two parts: its decay and beta once the current
-    // item's elementwise phase is done, its k and q one phase later (load_kq), once the
-    // pairwise products have consumed the current row operands. A single burst of all
-    // of them together with the current item's stores held the CU's memory pipeline
-    // (64 KB of loads and 32 KB of stores per workgroup): one part is 1.9 % faster per call.
+    // The next item's inputs load in parts rather than in one burst, which together with
+    // the current item's stores held the CU's vector-memory pipeline (64 KB of loads and
+    // 32 KB of stores per workgroup): its beta and the decay of channel block cb right
+    // after the current item stores its K.e^G and Q.e^G fragments of block cb (the
+    // elementwise phase), its k and q once the pairwise products have consumed the
+    // current row operands (load_kq). load() takes an item's inputs at once.
     __device__ __forceinline__ void load_gates(const PrefillArgs &a, const PrepItem &it, bool ok, int tr, int g) {
         valid = ok && tr < it.nt;
         const size_t t = static_cast<size_t>(it.t0 + (valid ? tr : 0));
@@ -282,6 +283,26 @@ struct PrepRaw {
             }
         }
         // raw bits: converting here would make the wave wait for the load at once
+        if (a.by) betaw = static_cast<const bf16_t *>(a.by)[tok];
+        else betaw = reinterpret_cast<const uint32_t *>(a.beta)[tok];
+    }
+    // the decay of channel block cb only (with valid as set by load_gates_meta)
+    __device__ __forceinline__ void load_gate_block(const PrefillArgs &a, const PrepItem &it, int tr, int g, int cb) {
+        const size_t t = static_cast<size_t>(it.t0 + (valid ? tr : 0));
+        const size_t row = (t * a.H + it.h) * K;
+        const int ch = 32 * cb + 16 * (g & 1) + 8 * (g >> 1);
+        if constexpr (GX) {
+            xv[cb] = *reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.gx) + row + ch);
+        } else {
+            gv[cb][0] = *reinterpret_cast<const float4 *>(a.g + row + ch);
+            gv[cb][1] = *reinterpret_cast<const float4 *>(a.g + row + ch + 4);
+        }
+    }
+    // valid and beta of an item
+    __device__ __forceinline__ void load_gates_meta(const PrefillArgs &a, const PrepItem &it, bool ok, int tr) {
+        valid = ok && tr < it.nt;
+        const size_t t = static_cast<size_t>(it.t0 + (valid ? tr : 0));
+        const size_t tok = t * a.H + it.h;
         if (a.by) betaw = static_cast<const bf16_t *>(a.by)[tok];
         else betaw = reinterpret_cast<const uint32_t *>(a.beta)[tok];
     }
@@ -505,6 +526,10 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
     if (tid < K) store_stream(reinterpret_cast<float *>(rec + R::GAM) + tid, sm.u.a.fac[18][tid]);
 
     // ---- elementwise: decayed operands
+    {
+        const int un = u + static_cast<int>(gridDim.x);
+        nx = prep_item(a, off, un < total ? un : 0);
+    }
     half8 kr[NCB], qr[NCB];
     // this lane's 8 channels of a 32-channel block (chain order) from a per-channel table row
     auto row8 = [&](const float *rowp, int cb, float (&o)[8]) {
@@ -551,16 +576,13 @@ __global__ __launch_bounds__(256, kPrepWgsPerCu) void prep_kernel(PrefillArgs a,
         }
         store_stream(reinterpret_cast<half8 *>(rec + R::KEXP + ((w * NCB + cb) * 64 + l) * 16), kexp);
         store_stream(reinterpret_cast<half8 *>(rec + R::QG + ((w * NCB + cb) * 64 + l) * 16), qg);
+        // the next item's beta and block cb of its decay (this item's are unpacked)
+        if (cb == 0) raw.load_gates_meta(a, nx, u + static_cast<int>(gridDim.x) < total, tr);
+        raw.load_gate_block(a, nx, tr, g, cb);
         sm.u.a.colv[vblk(w, w)][cb][l] = cv0;
         if (w + 1 < 4) sm.u.a.colv[vblk(w + 1, w)][cb][l] = cv1;
         if (w + 2 < 4) sm.u.a.colv[vblk(w + 2, w)][cb][l] = cv2;
         if (w == 0) sm.u.a.colv[vblk(3, 0)][cb][l] = cv3;
-    }
-    // the next item's decay and beta load from here on (this item's are no longer held)
-    {
-        const int un = u + static_cast<int>(gridDim.x);
-        nx = prep_item(a, off, un < total ? un : 0);
-        raw.load_gates(a, nx, un < total, tr, g);
     }
     __syncthreads();
 
